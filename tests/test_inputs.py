@@ -1,0 +1,109 @@
+"""The seeded workload generators: shapes, determinism and the stated recipe."""
+import numpy as np
+import torch
+
+from verify_pass_rejection_amd import inputs as I
+
+
+def small(name, **kw):
+    w = I.WORKLOADS[name]
+    base = dict(ctx=min(w.ctx, 40), V=min(w.V, 500), B=min(w.B, 4))
+    base.update(kw)
+    return w.with_(**base)
+
+
+def test_reference_workload_shapes():
+    W = I.WORKLOADS
+    assert (W["tiny_chain"].B, W["tiny_chain"].N, W["tiny_chain"].Hq, W["tiny_chain"].D,
+            W["tiny_chain"].ctx, W["tiny_chain"].V) == (1, 4, 8, 64, 256, 1024)
+    assert (W["llama3_8b_chain"].N, W["llama3_8b_chain"].Hq, W["llama3_8b_chain"].Hkv,
+            W["llama3_8b_chain"].V) == (5, 32, 8, 128256)
+    assert (W["eagle2_tree"].B, W["eagle2_tree"].T, len(W["eagle2_tree"].tree_widths) - 1) == (8, 64, 6)
+    assert (W["medusa70b_tree"].B, W["medusa70b_tree"].T, W["medusa70b_tree"].Hq) == (32, 42, 64)
+    assert (W["large_batch_chain"].B, W["large_batch_chain"].N, W["large_batch_chain"].ctx,
+            W["large_batch_chain"].V) == (64, 8, 32768, 152064)
+
+
+def test_attention_inputs_are_deterministic_and_typed():
+    w = small("llama3_8b_chain")
+    a = I.make_attention_inputs(w)
+    b = I.make_attention_inputs(w)
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)
+    q, k, v = a
+    assert q.dtype == torch.bfloat16 and q.shape == (w.B, w.T, w.Hq, w.D)
+    assert k.shape == (w.B, w.Hkv, w.ctx + w.T, w.D) and v.shape == k.shape
+    assert abs(float(k.float().std()) - 1.0) < 0.05
+    assert not torch.equal(k, v)
+
+
+def test_uniforms_are_exact_multiples_of_2_pow_minus_24():
+    g = torch.Generator().manual_seed(0)
+    u = I.uniforms((100000,), g, "cpu").double()
+    k = u * (1 << 24)
+    assert torch.equal(k, k.round()) and k.min() >= 1 and k.max() <= (1 << 24) - 1
+
+
+def test_chain_inputs_recipe():
+    w = small("tiny_chain", B=64, V=1024)
+    d = I.make_chain_inputs(w)
+    assert d["target_logits"].shape == (64, 5, 1024)
+    assert d["draft_logits"].shape == (64, 4, 1024)
+    noise = d["draft_logits"] - d["target_logits"][:, :4]
+    assert abs(float(noise.std()) - 0.5) < 0.01
+    assert abs(float(d["target_logits"].std()) - 2.0) < 0.02
+    assert d["draft_tokens"].dtype == torch.int32
+    assert int(d["draft_tokens"].min()) >= 0 and int(d["draft_tokens"].max()) < 1024
+    # Gumbel-max drafts follow q: the drafted token's q-mass averages well above uniform
+    q = torch.softmax(d["draft_logits"].double(), -1)
+    qx = q.gather(-1, d["draft_tokens"].long()[..., None])
+    assert float(qx.mean()) > 20.0 / 1024
+
+
+def test_eagle2_tree_shape():
+    w = small("eagle2_tree")
+    d = I.make_tree_inputs(w)
+    par = d["parents"].numpy()
+    widths = w.tree_widths
+    starts = np.cumsum((0,) + widths)
+    for b in range(w.B):
+        assert par[b, 0] == -1
+        for depth in range(1, len(widths)):
+            for i in range(starts[depth], starts[depth + 1]):
+                assert starts[depth - 1] <= par[b, i] < starts[depth]
+    assert not np.array_equal(par[0], par[1])          # a fresh tree per sequence
+
+
+def test_medusa_tree_shape():
+    w = small("medusa70b_tree")
+    d = I.make_tree_inputs(w)
+    par = d["parents"].numpy()
+    assert np.all(par == par[0])                       # one tree for the batch
+    p = list(par[0])
+    assert p[0] == -1 and all(0 <= p[i] < i for i in range(1, len(p)))
+    depth = [0] * len(p)
+    for i in range(1, len(p)):
+        depth[i] = depth[p[i]] + 1
+    assert max(depth) == 4
+    kids = {}
+    for i in range(1, len(p)):
+        kids.setdefault(p[i], []).append(i)
+    for n, ch in kids.items():
+        assert len(ch) <= w.tree_widths[depth[n]]
+
+
+def test_tree_planting_rate():
+    w = small("eagle2_tree", B=8, V=3000)
+    d = I.make_tree_inputs(w)
+    z, tok, par = d["target_logits"], d["tokens"], d["parents"]
+    hits = total = 0
+    for b in range(w.B):
+        seen = set()
+        for i in range(1, w.T):
+            p = int(par[b, i])
+            if p in seen:
+                continue
+            seen.add(p)                                # lowest-id child only
+            total += 1
+            hits += int(z[b, p, int(tok[b, i])] == I.PLANT_SIGMAS * w.target_sd)
+    assert 0.6 < hits / total < 0.95
