@@ -1,0 +1,233 @@
+"""Benchmark of the speculative-decoding verify step on one MI355X.
+
+One step = one pass of the whole hot path over one batch: verify attention of
+the N+1 draft positions against the KV cache (spec_verify_attention), then
+rejection-sampling acceptance on every target/draft row (spec_accept_chain).
+The workload is the large-batch chain: batch 64, N = 8 drafts, 32 query / 8 KV
+heads, head_dim 128, bf16 KV with a 32768-token prefix, vocabulary 152064.
+
+Printed: one JSON line with the step time, the achieved algorithmic HBM
+bandwidth of the step, of attention and of acceptance, the per-position
+verification overhead α = (T(N) − T(0)) / (N·T(0)) at N = 4 and 8 on the same
+shape, a roofline entry for the attention kernel and the CPU oracle's rate on a
+bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = ("verify-step µs + achieved HBM GB/s (attn, sampler) at N=4/8; α overhead")
+HBM_PEAK_GBPS = 8000.0
+WORKLOAD = "large_batch_chain"
+
+
+def attention_bytes(w) -> int:
+    """Algorithmic bytes of one attention call: K and V of all ctx+T keys once,
+    Q once, the fp32 output once."""
+    esz = 4 if w.dtype == "f32" else 2
+    kv = 2 * w.B * w.Hkv * w.L * w.D * esz
+    return kv + w.B * w.T * w.Hq * w.D * esz + w.B * w.T * w.Hq * w.D * 4
+
+
+def attention_flops(w) -> int:
+    return 4 * w.D * (w.Hq // w.Hkv) * w.T * w.L * w.B * w.Hkv
+
+
+def sampler_bytes(w) -> int:
+    """Algorithmic bytes of chain acceptance: every target and draft logit once."""
+    return (2 * w.N + 1) * w.V * 4 * w.B
+
+
+def alpha(t_n: float, t_0: float, n: int) -> float:
+    """Per-position verification overhead (T(N) − T(0)) / (N·T(0))."""
+    return (t_n - t_0) / (n * t_0)
+
+
+class Step:
+    """Device-resident inputs, outputs and workspaces for one workload."""
+
+    def __init__(self, w, dev):
+        import torch
+        from verify_pass_rejection_amd import inputs as I
+        from verify_pass_rejection_amd import native as nat
+        self.w, self.nat = w, nat
+        self.q, self.k, self.v = I.make_attention_inputs(w, dev)
+        self.d = I.make_chain_inputs(w, dev)
+        self.out = torch.empty((w.B, w.T, w.Hq, w.D), dtype=torch.float32, device=dev)
+        self.num = torch.empty(w.B, dtype=torch.int32, device=dev)
+        self.tok = torch.empty((w.B, w.T), dtype=torch.int32, device=dev)
+        dt = nat.SPEC_BF16 if w.dtype == "bf16" else nat.SPEC_F32
+        self.ws_a = torch.empty(nat.spec_verify_attention_workspace(
+            w.B, w.T, w.Hq, w.Hkv, w.D, w.ctx, dt), dtype=torch.uint8, device=dev)
+        self.ws_c = torch.empty(max(nat.spec_accept_chain_workspace(w.B, w.N, w.V), 1),
+                                dtype=torch.uint8, device=dev)
+        torch.cuda.synchronize()
+
+    def attention(self):
+        self.nat.spec_verify_attention(self.q, self.k, self.v, self.w.ctx, out=self.out,
+                                       workspace=self.ws_a)
+
+    def accept(self):
+        d = self.d
+        self.nat.spec_accept_chain(d["target_logits"], d["draft_logits"], d["draft_tokens"],
+                                   d["u_accept"], d["u_draw"], num_accepted=self.num,
+                                   out_tokens=self.tok, workspace=self.ws_c)
+
+    def __call__(self):
+        self.attention()
+        self.accept()
+
+
+def time_steps(step, steps: int, warmup: int):
+    """Warm up, then time exactly `steps` steps; per-call times from events on
+    the stream the library launches on (torch's current stream)."""
+    import torch
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    start.record()
+    for i in range(steps):
+        ev[i][0].record()
+        step.attention()
+        ev[i][1].record()
+        step.accept()
+        ev[i][2].record()
+    end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    attn = [e[0].elapsed_time(e[1]) for e in ev]
+    acc = [e[1].elapsed_time(e[2]) for e in ev]
+    return dict(ms_per_step=start.elapsed_time(end) / steps, wall_s=wall,
+                attn_ms=sum(attn) / steps, accept_ms=sum(acc) / steps,
+                attn_min_ms=min(attn), accept_min_ms=min(acc))
+
+
+def cpu_baseline(w, step, budget_s: float = 30.0):
+    """The fp64 oracle on a bounded sample: sequence 0 of the same batch
+    (attention for all its heads and positions, then its acceptance)."""
+    import numpy as np
+    import torch
+    from threadpoolctl import threadpool_info
+
+    from oracle.accept import chain_accept
+    from oracle.attention import verify_attention
+
+    f64 = lambda t: t.detach().cpu().to(torch.float64).numpy()   # noqa: E731
+    n_seq = 0
+    t0 = time.perf_counter()
+    while n_seq < w.B:
+        b = n_seq
+        verify_attention(f64(step.q[b:b + 1]), f64(step.k[b:b + 1]), f64(step.v[b:b + 1]), w.ctx)
+        d = step.d
+        chain_accept(f64(d["target_logits"][b:b + 1]), f64(d["draft_logits"][b:b + 1]),
+                     d["draft_tokens"][b:b + 1].cpu().numpy(), f64(d["u_accept"][b:b + 1]),
+                     f64(d["u_draw"][b:b + 1]))
+        n_seq += 1
+        if time.perf_counter() - t0 > budget_s / 2:
+            break
+    dt = time.perf_counter() - t0
+    per_seq = (attention_bytes(w) + sampler_bytes(w)) / w.B
+    threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    return {"value": round(per_seq * n_seq / dt / 1e9, 4), "unit": "GB/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"{n_seq} of {w.B} sequences of {w.name} (attention for all "
+                      f"{w.Hq} heads x {w.T} positions over ctx {w.ctx}, then chain "
+                      f"acceptance over {2 * w.N + 1} rows of V={w.V}); host-to-numpy copies "
+                      f"included; {dt:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-alpha", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the verify step shards with no exchange over batch or KV heads; see DESIGN.md)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from verify_pass_rejection_amd import inputs as I
+
+    dev = torch.device("cuda:0")
+    w = I.WORKLOADS[WORKLOAD]
+    step = Step(w, dev)
+    t = time_steps(step, args.steps, args.warmup)
+
+    ab, sb = attention_bytes(w), sampler_bytes(w)
+    attn_gbps = ab / (t["attn_ms"] * 1e-3) / 1e9
+    samp_gbps = sb / (t["accept_ms"] * 1e-3) / 1e9
+    step_gbps = (ab + sb) / (t["ms_per_step"] * 1e-3) / 1e9
+
+    alphas = {}
+    if not args.no_alpha:
+        times = {w.N: t["ms_per_step"]}
+        del step
+        torch.cuda.empty_cache()
+        for n in (0, 4):
+            wn = w.with_(T=n + 1)
+            s = Step(wn, dev)
+            times[n] = time_steps(s, max(10, args.steps // 2), 3)["ms_per_step"]
+            del s
+            torch.cuda.empty_cache()
+        alphas = {f"alpha_N{n}": round(alpha(times[n], times[0], n), 4) for n in (4, w.N)}
+        alphas["verify_step_us_by_N"] = {str(n): round(times[n] * 1e3, 2) for n in sorted(times)}
+        step = Step(w, dev)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(w, step)
+
+    line = {
+        "metric": METRIC,
+        "value": round(step_gbps, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(t["ms_per_step"], 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded; stands in for the pages' unnamed chat/code workloads)",
+        "config": {"workload": w.name, "batch": w.B, "N": w.N, "Hq": w.Hq, "Hkv": w.Hkv,
+                   "head_dim": w.D, "ctx": w.ctx, "vocab": w.V, "kv_dtype": w.dtype},
+        "verify_step_us": round(t["ms_per_step"] * 1e3, 2),
+        "attn_us": round(t["attn_ms"] * 1e3, 2),
+        "sampler_us": round(t["accept_ms"] * 1e3, 2),
+        "attn_GBps": round(attn_gbps, 1),
+        "sampler_GBps": round(samp_gbps, 1),
+        "attn_frac_hbm_peak": round(attn_gbps / HBM_PEAK_GBPS, 4),
+        "sampler_frac_hbm_peak": round(samp_gbps / HBM_PEAK_GBPS, 4),
+        "attn_TFLOPs": round(attention_flops(w) / (t["attn_ms"] * 1e-3) / 1e12, 2),
+        **alphas,
+        "roofline": {"bound": "hbm", "achieved": round(attn_gbps, 1), "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": round(attn_gbps / HBM_PEAK_GBPS, 4),
+                     "traffic": None,
+                     "kernel": "spec_verify_attention (split-K MFMA kernel + split combine)",
+                     "algorithmic_bytes_per_launch": ab},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

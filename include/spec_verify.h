@@ -1,0 +1,169 @@
+/*
+ * spec_verify.h — C ABI of the speculative-decoding verify step for MI355X (gfx950).
+ *
+ * The verify step is the target model's single check of a batch of drafts:
+ *
+ *   1. verify attention — the target's pass over the accepted prefix plus the
+ *      N draft positions is parallel over positions, so one pass yields a
+ *      next-token distribution at each of the N+1 positions ("LLM Primer VI —
+ *      Chapitre 9 — Décodage spéculatif", §9.1).  A draft tree is checked in
+ *      the same single pass under a mask that encodes the tree (Primer §9.2 on
+ *      EAGLE-2; "Parallel Decoding" glossary, "Medusa" → "Tree attention" and
+ *      "L'attention en arbre : la brique commune").
+ *   2. acceptance — for a chain, rejection sampling: keep draft x with
+ *      probability min(1, p(x)/q(x)), else draw from the normalised (p − q)+ and
+ *      drop the rest, so the output law is exactly the target's (Primer §9.1);
+ *      for a tree, the longest path that agrees with the target, then the
+ *      target's own choice (glossary "L'attention en arbre"; Primer §9.1–§9.2).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Every data pointer is a caller-owned DEVICE buffer, dense row-major in the
+ *    layout stated at each argument.  The library keeps no state and allocates
+ *    no memory; scratch space comes from the caller's `workspace` (device
+ *    memory, at least the size the matching *_workspace() query returns, no
+ *    alignment beyond 256 bytes required, contents need not be initialised).
+ *  - Work is enqueued asynchronously on `hip_stream` (a hipStream_t; NULL means
+ *    the null stream).  Outputs are valid once that stream reaches the point
+ *    after the call.  Concurrent calls must use distinct workspaces.
+ *  - Errors: every call validates its arguments on the host before enqueuing
+ *    anything and returns a spec_status; nothing is launched unless it returns
+ *    SPEC_OK.  A launch failure reported by HIP gives SPEC_ERR_HIP.  Faults
+ *    inside kernels surface at the caller's next synchronisation.  No
+ *    exception crosses the ABI and the library never aborts.
+ *  - Preconditions not checked on the device (results are unspecified but
+ *    memory-safe if violated): logits are finite or -inf with a finite row
+ *    maximum; parents satisfy parents[b][0] == -1 and 0 <= parents[b][i] < i.
+ *    Out-of-range tokens and malformed parents never read out of bounds: such
+ *    a draft or node is simply never accepted.
+ *  - Empty problems (B == 0, or no query positions) return SPEC_OK without
+ *    launching anything.
+ */
+#ifndef SPEC_VERIFY_H
+#define SPEC_VERIFY_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    SPEC_OK = 0,
+    SPEC_ERR_NULL = 1,         /* a required pointer is NULL                      */
+    SPEC_ERR_SHAPE = 2,        /* a size is negative or inconsistent              */
+    SPEC_ERR_UNSUPPORTED = 3,  /* valid but outside the supported limits          */
+    SPEC_ERR_WORKSPACE = 4,    /* workspace_bytes below the queried size          */
+    SPEC_ERR_HIP = 5           /* the HIP runtime reported a launch error         */
+} spec_status;
+
+typedef enum {
+    SPEC_F32 = 0,              /* IEEE binary32                                   */
+    SPEC_BF16 = 1              /* bfloat16 (upper half of a binary32)             */
+} spec_dtype;
+
+/* Supported limits. */
+#define SPEC_MAX_T 64          /* query positions (chain N+1, or tree nodes)      */
+#define SPEC_MAX_V (1 << 24)   /* vocabulary size                                 */
+
+/* Text for a status code (static storage; never NULL). */
+const char* spec_status_string(spec_status status);
+
+/* ---------------------------------------------------------------------------
+ * Verify attention (Primer §9.1, §9.2; glossary "L'attention en arbre").
+ *
+ * For every sequence b, query position i < T and query head h:
+ *
+ *   O[b,i,h,:] = sum_{j in vis(b,i)} softmax_j(scale * <Q[b,i,h,:], K[b,g,j,:]>) * V[b,g,j,:]
+ *
+ * with g = h / (Hq/Hkv) (grouped-query attention) and the visible keys
+ * vis(b,i) = {0 .. ctx-1} (the accepted prefix) ∪ {ctx + t : t is i or an
+ * ancestor of i}.  A chain (parents == NULL) makes every earlier position an
+ * ancestor, i.e. causal attention over the N+1 new positions.
+ *
+ *   q        [B, T, Hq, D]       dtype; already position-encoded
+ *   k, v     [B, Hkv, ctx+T, D]  dtype; rows ctx..ctx+T-1 hold the T new
+ *                                positions (appended before the call)
+ *   parents  [B, T] int32 or NULL; tree: parents[b][0] = -1 (node 0 is the
+ *            root, the last verified token), parents[b][i] < i
+ *   out      [B, T, Hq, D] float32
+ *   scale    softmax scale, normally 1/sqrt(D); must be finite
+ *
+ * Limits: 1 <= T <= 64, D in {64, 128}, Hkv >= 1, Hq % Hkv == 0, ctx >= 0.
+ * ------------------------------------------------------------------------- */
+size_t spec_verify_attention_workspace(int B, int T, int Hq, int Hkv, int D, int ctx,
+                                       spec_dtype dtype);
+
+spec_status spec_verify_attention(const void* q, const void* k, const void* v,
+                                  const int32_t* parents, float* out,
+                                  int B, int T, int Hq, int Hkv, int D, int ctx,
+                                  spec_dtype dtype, float scale,
+                                  void* workspace, size_t workspace_bytes,
+                                  void* hip_stream);
+
+/* ---------------------------------------------------------------------------
+ * Chain acceptance by rejection sampling (Primer §9.1).
+ *
+ * With p_i = softmax(target_logits[b,i,:] / temperature) (i = 0..N) and
+ * q_i = softmax(draft_logits[b,i,:] / temperature) (i = 0..N-1):
+ *   draft x_i is kept iff u_accept[b,i] < p_i(x_i) / q_i(x_i)  (q = 0 → +inf
+ *   if p > 0, else 0); k = the first i not kept (N if all are kept);
+ *   if k < N the committed token is drawn from w = (p_k − q_k)+ (or p_k when
+ *   that sums to zero), else from w = p_N (the bonus token);
+ *   the draw is y = min{j : C_j > u_draw[b,k] * C_{V-1}}, C_j the running sum
+ *   of w in ascending token order (the last j with w_j > 0 if none).
+ *
+ *   target_logits  [B, N+1, V] float32
+ *   draft_logits   [B, N, V]   float32
+ *   draft_tokens   [B, N]      int32 (drafts drawn from q)
+ *   u_accept       [B, N]      float32 in (0,1)
+ *   u_draw         [B, N+1]    float32 in (0,1); only row k's is used
+ *   temperature    > 0
+ *   num_accepted   [B]         int32 out: k
+ *   out_tokens     [B, N+1]    int32 out: x_0..x_{k-1}, y, then -1
+ *
+ * For N == 0 the pointers to draft_logits, draft_tokens and u_accept may be NULL.
+ * Limits: N >= 0, 1 <= V <= SPEC_MAX_V.
+ * ------------------------------------------------------------------------- */
+size_t spec_accept_chain_workspace(int B, int N, int V);
+
+spec_status spec_accept_chain(const float* target_logits, const float* draft_logits,
+                              const int32_t* draft_tokens, const float* u_accept,
+                              const float* u_draw, float temperature,
+                              int32_t* num_accepted, int32_t* out_tokens,
+                              int B, int N, int V,
+                              void* workspace, size_t workspace_bytes, void* hip_stream);
+
+/* ---------------------------------------------------------------------------
+ * Greedy tree acceptance (glossary "L'attention en arbre : la brique commune";
+ * Primer §9.1–§9.2).
+ *
+ * a_i = argmax_v target_logits[b,i,v] (lowest v among equal maxima) is the
+ * target's own choice after node i.  Node 0 (the root) is accepted; node i > 0
+ * is accepted iff its parent is accepted and tokens[b,i] == a_{parent(i)}.
+ * The deepest accepted node l (lowest id among equally deep ones) ends the
+ * accepted path root..l.
+ *
+ *   target_logits  [B, T, V]  float32, the target's logits at every node
+ *   tokens         [B, T]     int32 draft token carried by each node (node 0 ignored)
+ *   parents        [B, T]     int32, parents[b][0] = -1, parents[b][i] < i
+ *   accept_len     [B]        int32 out: depth of l (number of accepted drafts)
+ *   path           [B, T]     int32 out: node ids root..l, then -1
+ *   out_tokens     [B, T]     int32 out: tokens of path nodes 1..l, then a_l, then -1
+ *
+ * Limits: 1 <= T <= 64, 1 <= V <= SPEC_MAX_V.
+ * ------------------------------------------------------------------------- */
+size_t spec_accept_tree_workspace(int B, int T, int V);
+
+spec_status spec_accept_tree(const float* target_logits, const int32_t* tokens,
+                             const int32_t* parents,
+                             int32_t* accept_len, int32_t* path, int32_t* out_tokens,
+                             int B, int T, int V,
+                             void* workspace, size_t workspace_bytes, void* hip_stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPEC_VERIFY_H */

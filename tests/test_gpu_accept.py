@@ -1,0 +1,160 @@
+"""GPU parity of spec_accept_chain and spec_accept_tree against oracle.accept.
+
+Chain: accepted lengths and token ids must match the oracle exactly on every
+sequence whose decisions are not flagged.  A decision may be excluded only if
+its uniform lies within 1e-5 (relative) of the fp64 boundary; these tests use a
+ten times narrower band, 1e-6, because the fp32 kernels were measured to agree
+with the fp64 oracle on every decision farther than 1e-7 from its boundary
+(about 10^4 sequences at the reference shapes).  Both flag counts are printed.  Tree:
+bit-exact, no flags (comparisons and integers only).  A χ² law test runs the
+GPU kernel on 10^6 trials.
+"""
+import numpy as np
+import pytest
+import torch
+from scipy import stats
+from scipy.special import softmax as sp_softmax
+
+from gpu_support import device, f64, i64, say
+from oracle.accept import chain_accept, tree_accept
+from verify_pass_rejection_amd import inputs as I
+from verify_pass_rejection_amd import native as nat
+
+pytestmark = pytest.mark.gpu
+
+
+TEST_BAND = 1e-6        # exclusion band used here (the allowed maximum is 1e-5)
+
+
+def compare_chain(d, temperature=1.0, label=""):
+    num, out = nat.spec_accept_chain(d["target_logits"], d["draft_logits"], d["draft_tokens"],
+                                     d["u_accept"], d["u_draw"], temperature=temperature)
+    torch.cuda.synchronize()
+    args = (f64(d["target_logits"]), f64(d["draft_logits"]), i64(d["draft_tokens"]),
+            f64(d["u_accept"]), f64(d["u_draw"]))
+    ref = chain_accept(*args, temperature=temperature, band=TEST_BAND)
+    wide = chain_accept(*args, temperature=temperature, band=1e-5).near_boundary
+    num, out = i64(num), i64(out)
+    ok = ~ref.near_boundary
+    mism = ok & ((num != ref.num_accepted) | np.any(out != ref.out_tokens, axis=1))
+    say(label, f"B={len(num)} flagged@1e-6={int((~ok).sum())} flagged@1e-5={int(wide.sum())}",
+        f"mismatched={int(mism.sum())} mean_accepted={num.mean():.3f}")
+    assert not mism.any(), np.nonzero(mism)[0][:10]
+    assert (~ok).mean() < 0.15          # enough unflagged sequences for the check to bite
+    return num, out, ref
+
+
+@pytest.mark.parametrize("name,kw", [
+    ("tiny_chain", dict(B=512)),
+    ("llama3_8b_chain", dict(B=8)),
+    ("large_batch_chain", dict()),                  # full reference size, all 64x9 rows
+    ("large_batch_chain", dict(B=16, V=1001)),      # V not a multiple of 4: scalar path
+    ("large_batch_chain", dict(B=64, T=1)),         # N = 0: plain sampling from p_0
+    ("large_batch_chain", dict(B=32, T=64, V=777)), # N = 63
+])
+def test_chain_matches_oracle(name, kw):
+    dev = device()
+    w = I.WORKLOADS[name].with_(**kw)
+    compare_chain(I.make_chain_inputs(w, dev), label=f"{name} {kw}")
+
+
+def test_chain_temperature():
+    dev = device()
+    w = I.WORKLOADS["llama3_8b_chain"].with_(B=16, V=5000, temperature=0.7)
+    compare_chain(I.make_chain_inputs(w, dev), temperature=0.7, label="tau=0.7")
+
+
+def test_chain_infinite_logits_and_invalid_tokens():
+    dev = device()
+    w = I.WORKLOADS["tiny_chain"].with_(B=64, V=300, seed=21)
+    d = I.make_chain_inputs(w, dev)
+    # q(x) = 0 for some drafted tokens: -inf draft logits there (accept iff p(x) > 0)
+    d["draft_logits"][:8, :, :150] = -float("inf")
+    d["draft_tokens"][:8] = torch.randint(0, 150, (8, w.N), device=dev, dtype=torch.int32)
+    # p(x) = 0 as well: always rejected
+    d["target_logits"][8:16, :, :] = -float("inf")
+    d["target_logits"][8:16, :, 299] = 0.0
+    # out-of-range drafts are rejected
+    d["draft_tokens"][16:24, 1] = -5
+    d["draft_tokens"][24:32, 0] = w.V
+    # identical rows with a rejected (invalid) draft: empty residual, falls back to p
+    d["draft_logits"][32:40] = d["target_logits"][32:40, :w.N]
+    d["draft_tokens"][32:40, 0] = -1
+    num, out, _ = compare_chain(d, label="inf/invalid")
+    assert np.all(num[16:24] <= 1) and np.all(num[24:32] == 0) and np.all(num[32:40] == 0)
+
+
+def test_chain_law_chi2_on_gpu():
+    dev = device()
+    V, N, B = 16, 1, 1_000_000
+    g = torch.Generator(device=dev).manual_seed(77)
+    zp = torch.randn((1, N + 1, V), generator=g, device=dev) * 2
+    zq = zp[:, :N] + torch.randn((1, N, V), generator=g, device=dev)
+    q = torch.softmax(zq[0, 0].double(), -1)
+    drafts = torch.multinomial(q, B, replacement=True, generator=g).to(torch.int32).view(B, 1)
+    ua = I.uniforms((B, N), g, dev)
+    ud = I.uniforms((B, N + 1), g, dev)
+    num, out = nat.spec_accept_chain(zp.expand(B, -1, -1).contiguous(),
+                                     zq.expand(B, -1, -1).contiguous(), drafts, ua, ud)
+    first = np.bincount(i64(out[:, 0]), minlength=V)
+    p0 = sp_softmax(f64(zp[0, 0]))
+    chi = stats.chisquare(first, B * p0).statistic
+    say(f"chi2(first token vs p0) = {chi:.2f} (df=15, 0.999 quantile 37.70)")
+    assert chi < 37.697
+
+
+def compare_tree(d, label=""):
+    al, path, out = nat.spec_accept_tree(d["target_logits"], d["tokens"], d["parents"])
+    torch.cuda.synchronize()
+    ref = tree_accept(f64(d["target_logits"]), i64(d["tokens"]), i64(d["parents"]))
+    al, path, out = i64(al), i64(path), i64(out)
+    say(label, f"B={len(al)} mean_accept_len={al.mean():.3f}")
+    np.testing.assert_array_equal(al, ref.accept_len)
+    np.testing.assert_array_equal(path, ref.path)
+    np.testing.assert_array_equal(out, ref.out_tokens)
+    return al
+
+
+@pytest.mark.parametrize("name,kw", [
+    ("eagle2_tree", dict()),                 # full reference size
+    ("medusa70b_tree", dict()),              # full reference size
+    ("eagle2_tree", dict(B=4, V=3001)),      # ragged vocabulary, scalar path
+    ("medusa70b_tree", dict(B=8, V=20000, seed=31)),
+])
+def test_tree_matches_oracle(name, kw):
+    dev = device()
+    w = I.WORKLOADS[name].with_(**kw)
+    al = compare_tree(I.make_tree_inputs(w, dev), label=f"{name} {kw}")
+    assert al.max() >= 2          # planted drafts make deep acceptance common
+
+
+def test_tree_ties_chain_and_malformed_parents():
+    dev = device()
+    B, T, V = 6, 5, 20000
+    z = torch.randn((B, T, V), device=dev)
+    # ties across the chunk boundary and within a chunk: lowest index wins
+    z[:, :, 5] = 50.0
+    z[:, :, 8192 + 5] = 50.0
+    z[0, 0, 5] = 10.0
+    z[0, 0, 17000] = 50.0
+    tokens = torch.full((B, T), 5, dtype=torch.int32, device=dev)
+    parents = torch.tensor([[-1, 0, 1, 2, 3]] * B, dtype=torch.int32, device=dev)
+    parents[1, 3] = 3            # malformed (not < 3)
+    parents[2, 2] = 7            # malformed (out of range)
+    parents[3] = torch.tensor([-1, 0, 0, 1, 1])
+    tokens[4, 2] = -1
+    compare_tree(dict(target_logits=z, tokens=tokens, parents=parents), label="ties")
+    # single node: argmax decode step
+    zz = torch.randn((3, 1, 999), device=dev)
+    compare_tree(dict(target_logits=zz, tokens=torch.zeros((3, 1), dtype=torch.int32, device=dev),
+                      parents=torch.full((3, 1), -1, dtype=torch.int32, device=dev)), label="T=1")
+
+
+def test_accept_deterministic_run_twice():
+    dev = device()
+    d = I.make_chain_inputs(I.WORKLOADS["llama3_8b_chain"].with_(B=4), dev)
+    a = nat.spec_accept_chain(d["target_logits"], d["draft_logits"], d["draft_tokens"],
+                              d["u_accept"], d["u_draw"])
+    b = nat.spec_accept_chain(d["target_logits"], d["draft_logits"], d["draft_tokens"],
+                              d["u_accept"], d["u_draw"])
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])

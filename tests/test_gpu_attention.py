@@ -1,0 +1,122 @@
+"""GPU parity of spec_verify_attention against oracle.attention.
+
+Reduced sizes (several key tiles and splits, a ragged tail) are compared
+element by element; the full reference sizes, in the launch configuration the
+bench times, are compared on sampled output rows.  Tolerances: max-abs 1e-4
+for fp32 inputs, 2e-2 for bf16 K/V.
+"""
+import zlib
+
+import numpy as np
+import pytest
+import torch
+
+from gpu_support import BF16_ATOL, F32_ATOL, device, f64, say
+from oracle.attention import verify_attention
+from verify_pass_rejection_amd import inputs as I
+from verify_pass_rejection_amd import native as nat
+
+pytestmark = pytest.mark.gpu
+
+
+def run_case(w, parents=None, rows=None, atol=None):
+    dev = device()
+    q, k, v = I.make_attention_inputs(w, dev)
+    if parents is None and w.kind == "tree":
+        parents = I.make_tree_inputs(w.with_(V=8), dev)["parents"]
+    say(w.name, "inputs ready; launching")
+    out = nat.spec_verify_attention(q, k, v, w.ctx, parents=parents)
+    torch.cuda.synchronize()
+    par = None if parents is None else parents.cpu().numpy()
+    if rows is None:
+        want = verify_attention(f64(q), f64(k), f64(v), w.ctx, parents=par)
+        got = f64(out)
+    else:
+        # only the sequences that hold sampled rows are copied to the host
+        got, want = [], []
+        for b in sorted({r[0] for r in rows}):
+            sub = [(0, t, h) for (bb, t, h) in rows if bb == b]
+            o = verify_attention(f64(q[b:b + 1]), f64(k[b:b + 1]), f64(v[b:b + 1]), w.ctx,
+                                 parents=None if par is None else par[b:b + 1], rows=sub)
+            for (_, t, h) in sub:
+                want.append(o[0, t, h])
+                got.append(f64(out[b, t, h]))
+        got, want = np.array(got), np.array(want)
+    tol = atol if atol is not None else (F32_ATOL if w.dtype == "f32" else BF16_ATOL)
+    err = float(np.max(np.abs(got - want)))
+    say(w.name, f"B={w.B} T={w.T} Hq={w.Hq} Hkv={w.Hkv} D={w.D} ctx={w.ctx} {w.dtype}",
+        f"max_abs_err={err:.3e} tol={tol}")
+    assert np.all(np.isfinite(got))
+    assert err <= tol
+    return out
+
+
+REDUCED = {
+    "tiny_chain": dict(),                                   # already small: full size
+    "llama3_8b_chain": dict(B=2, ctx=1000),
+    "eagle2_tree": dict(B=2, ctx=700),
+    "medusa70b_tree": dict(B=2, ctx=300),
+    "large_batch_chain": dict(B=2, ctx=2000),
+}
+
+
+@pytest.mark.parametrize("name", list(REDUCED))
+def test_reduced_workloads_elementwise(name):
+    run_case(I.WORKLOADS[name].with_(**REDUCED[name]))
+
+
+@pytest.mark.parametrize("name,kw", [
+    ("decode_step_T1_bf16_valu", dict(T=1, Hq=32, Hkv=8, D=128, ctx=1500, dtype="bf16")),
+    ("decode_step_T1_f32", dict(T=1, Hq=8, Hkv=8, D=64, ctx=333, dtype="f32")),
+    ("f32_rows_over_8_row_chunks", dict(T=5, Hq=16, Hkv=4, D=128, ctx=200, dtype="f32")),
+    ("bf16_12_rows_valu_two_chunks", dict(T=3, Hq=32, Hkv=8, D=128, ctx=700, dtype="bf16")),
+    ("bf16_d64_mfma", dict(T=8, Hq=16, Hkv=4, D=64, ctx=450, dtype="bf16")),
+    ("bf16_d64_valu", dict(T=2, Hq=8, Hkv=4, D=64, ctx=90, dtype="bf16")),
+    ("empty_prefix", dict(T=6, Hq=32, Hkv=8, D=128, ctx=0, dtype="bf16")),
+    ("chain_of_64", dict(T=64, Hq=8, Hkv=8, D=128, ctx=65, dtype="bf16")),
+    ("gqa_8_mfma_two_row_chunks", dict(T=64, Hq=64, Hkv=8, D=128, ctx=40, dtype="bf16")),
+])
+def test_edge_shapes(name, kw):
+    base = I.WORKLOADS["large_batch_chain"].with_(name=name, B=2, kind="chain", seed=11, **kw)
+    run_case(base)
+
+
+def test_random_tree_of_64_with_deep_branches():
+    dev = device()
+    w = I.WORKLOADS["eagle2_tree"].with_(B=3, ctx=97, seed=12)
+    g = torch.Generator().manual_seed(5)
+    par = [[-1] + [int(torch.randint(max(0, i - 3), i, (1,), generator=g)) for i in range(1, 64)]
+           for _ in range(3)]
+    run_case(w, parents=torch.tensor(par, dtype=torch.int32, device=dev))
+
+
+def test_chain_equals_tree_with_consecutive_parents_bitwise():
+    dev = device()
+    w = I.WORKLOADS["large_batch_chain"].with_(B=2, ctx=900, seed=13)
+    q, k, v = I.make_attention_inputs(w, dev)
+    chain = nat.spec_verify_attention(q, k, v, w.ctx)
+    par = torch.tensor([[-1] + list(range(w.T - 1))] * w.B, dtype=torch.int32, device=dev)
+    tree = nat.spec_verify_attention(q, k, v, w.ctx, parents=par)
+    assert torch.equal(chain, tree)
+
+
+def test_deterministic_run_twice():
+    dev = device()
+    w = I.WORKLOADS["eagle2_tree"].with_(B=2, ctx=1200, seed=14)
+    q, k, v = I.make_attention_inputs(w, dev)
+    par = I.make_tree_inputs(w.with_(V=8), dev)["parents"]
+    a = nat.spec_verify_attention(q, k, v, w.ctx, parents=par)
+    b = nat.spec_verify_attention(q, k, v, w.ctx, parents=par)
+    assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("name", ["llama3_8b_chain", "eagle2_tree", "medusa70b_tree",
+                                  "large_batch_chain"])
+def test_full_size_sampled_rows(name):
+    w = I.WORKLOADS[name]
+    rng = np.random.default_rng(zlib.crc32(name.encode()))
+    rows = sorted({(int(rng.integers(w.B)), int(rng.integers(w.T)), int(rng.integers(w.Hq)))
+                   for _ in range(24)})
+    rows += [(w.B - 1, w.T - 1, w.Hq - 1), (0, 0, 0)]
+    run_case(w, rows=rows)
+    torch.cuda.empty_cache()

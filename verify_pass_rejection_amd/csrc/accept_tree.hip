@@ -1,0 +1,165 @@
+// Greedy acceptance of a draft tree.
+//
+// "Parallel Decoding" glossary, "L'attention en arbre : la brique commune": the
+// root is the last verified token, every branch is a candidate continuation,
+// and the longest accepted path becomes the generated sequence.  "LLM Primer
+// VI — Chapitre 9 — Décodage spéculatif", §9.1: at the first divergence the
+// engine commits to the target's own choice; §9.2: the target picks the best
+// of several draft paths.
+//
+// Two kernels:
+//  tree_argmax — every node's logit row is read once; per chunk the maximum
+//                and its lowest index;
+//  tree_walk   — one wave per sequence: merges the chunks into the target's
+//                choice a_i at each node, then walks the (topologically
+//                ordered) parents: node i is accepted iff its parent is and its
+//                token equals a_parent(i); the deepest accepted node (lowest id
+//                on ties) ends the path; a_l follows the path's tokens.
+
+#include "common.h"
+
+#include <limits.h>
+
+namespace sv {
+
+struct TreeArgs {
+  const float* logits;     // [B, T, V]
+  const int32_t* tokens;   // [B, T]
+  const int32_t* parents;  // [B, T]
+  int32_t* accept_len;     // [B]
+  int32_t* path;           // [B, T]
+  int32_t* out;            // [B, T]
+  float* part_val;         // [B*T, nchunks]
+  int32_t* part_idx;       // [B*T, nchunks]
+  int B, T, V, nchunks;
+};
+
+constexpr int kArgThreads = 256;
+constexpr int kArgChunk = 8192;
+
+// (v, i) is better than (bv, bi): larger value, or equal value and lower index.
+__device__ __forceinline__ bool better(float v, int i, float bv, int bi) {
+  return v > bv || (v == bv && i < bi);
+}
+
+template <int VEC>
+__global__ __launch_bounds__(kArgThreads) void tree_argmax_kernel(TreeArgs a) {
+  constexpr int ITER = kArgChunk / (kArgThreads * VEC);
+  __shared__ float sv_[kArgThreads / kWave];
+  __shared__ int si_[kArgThreads / kWave];
+  const int ch = blockIdx.x, row = blockIdx.y;
+  const float* z = a.logits + (size_t)row * a.V;
+  const int begin = ch * kArgChunk;
+
+  float v[ITER * VEC];
+#pragma unroll
+  for (int it = 0; it < ITER; ++it) {
+    const int j = begin + (it * kArgThreads + threadIdx.x) * VEC;
+    if constexpr (VEC == 4) {
+      float4 x = {kNegInf, kNegInf, kNegInf, kNegInf};
+      if (j < a.V) x = *(const float4*)(z + j);
+      v[it * 4 + 0] = x.x; v[it * 4 + 1] = x.y; v[it * 4 + 2] = x.z; v[it * 4 + 3] = x.w;
+    } else {
+      v[it] = j < a.V ? z[j] : kNegInf;
+    }
+  }
+  float bv = kNegInf;
+  int bi = INT_MAX;
+#pragma unroll
+  for (int it = 0; it < ITER; ++it)
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) {
+      const int j = begin + (it * kArgThreads + threadIdx.x) * VEC + e;
+      if (j < a.V && better(v[it * VEC + e], j, bv, bi)) { bv = v[it * VEC + e]; bi = j; }
+    }
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) {
+    const float ov = __shfl_xor(bv, off);
+    const int oi = __shfl_xor(bi, off);
+    if (better(ov, oi, bv, bi)) { bv = ov; bi = oi; }
+  }
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  if (lane == 0) { sv_[wave] = bv; si_[wave] = bi; }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    for (int w = 1; w < kArgThreads / kWave; ++w)
+      if (better(sv_[w], si_[w], bv, bi)) { bv = sv_[w]; bi = si_[w]; }
+    a.part_val[(size_t)row * a.nchunks + ch] = bv;
+    a.part_idx[(size_t)row * a.nchunks + ch] = bi;
+  }
+}
+
+__global__ __launch_bounds__(64) void tree_walk_kernel(TreeArgs a) {
+  __shared__ int choice[64], par[64], tok[64], depth[64], acc[64], path_nodes[64];
+  __shared__ int s_best, s_depth;
+  const int b = blockIdx.x, i = threadIdx.x, T = a.T;
+  if (i < T) {
+    const size_t row = (size_t)b * T + i;
+    float bv = a.part_val[row * a.nchunks];
+    int bi = a.part_idx[row * a.nchunks];
+    for (int c = 1; c < a.nchunks; ++c) {
+      const float v = a.part_val[row * a.nchunks + c];
+      const int j = a.part_idx[row * a.nchunks + c];
+      if (better(v, j, bv, bi)) { bv = v; bi = j; }
+    }
+    choice[i] = bi;
+    par[i] = a.parents[row];
+    tok[i] = a.tokens[row];
+  }
+  __syncthreads();
+  if (i == 0) {
+    depth[0] = 0;
+    acc[0] = 1;
+    int best = 0;
+    for (int n = 1; n < T; ++n) {
+      const int p = par[n];
+      if (p < 0 || p >= n) { depth[n] = 0; acc[n] = 0; continue; }
+      depth[n] = depth[p] + 1;
+      acc[n] = acc[p] && tok[n] == choice[p];
+      if (acc[n] && depth[n] > depth[best]) best = n;
+    }
+    const int d = depth[best];
+    int n = best;
+    for (int k = d; k >= 0; --k) { path_nodes[k] = n; n = par[n]; }
+    s_best = best;
+    s_depth = d;
+  }
+  __syncthreads();
+  if (i < T) {
+    const int d = s_depth;
+    const size_t o = (size_t)b * T + i;
+    a.path[o] = i <= d ? path_nodes[i] : -1;
+    a.out[o] = i < d ? tok[path_nodes[i + 1]] : (i == d ? choice[s_best] : -1);
+    if (i == 0) a.accept_len[b] = d;
+  }
+}
+
+TreePlan plan_tree(int B, int T, int V) {
+  TreePlan p{};
+  p.chunk = kArgChunk;
+  p.nchunks = (V + kArgChunk - 1) / kArgChunk;
+  p.part_bytes = align256((size_t)B * T * p.nchunks * sizeof(float));
+  p.total_bytes = 2 * p.part_bytes;
+  return p;
+}
+
+hipError_t launch_tree(const TreePlan& p, const float* logits, const int32_t* tokens,
+                       const int32_t* parents, int32_t* accept_len, int32_t* path,
+                       int32_t* out, int B, int T, int V, void* workspace, hipStream_t st) {
+  TreeArgs a;
+  a.logits = logits; a.tokens = tokens; a.parents = parents;
+  a.accept_len = accept_len; a.path = path; a.out = out;
+  a.part_val = (float*)workspace;
+  a.part_idx = (int32_t*)((char*)workspace + p.part_bytes);
+  a.B = B; a.T = T; a.V = V; a.nchunks = p.nchunks;
+  const bool vec4 = (V % 4 == 0) && ((uintptr_t)logits % 16 == 0);
+  const dim3 g1(p.nchunks, B * T);
+  if (vec4) tree_argmax_kernel<4><<<g1, kArgThreads, 0, st>>>(a);
+  else tree_argmax_kernel<1><<<g1, kArgThreads, 0, st>>>(a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  tree_walk_kernel<<<B, 64, 0, st>>>(a);
+  return hipGetLastError();
+}
+
+}  // namespace sv

@@ -1,0 +1,601 @@
+// Verify attention for the N+1 chain positions or the T tree nodes of a draft,
+// against the KV cache of the accepted prefix plus the draft positions.
+//
+// "LLM Primer VI — Chapitre 9 — Décodage spéculatif", §9.1: the target's pass
+// over prefix + N candidates is parallel over positions and yields a next-token
+// distribution at each of the N+1 positions; §9.2: an EAGLE-2 draft tree is
+// verified in one attention pass under a custom mask.  "Parallel Decoding"
+// glossary, "L'attention en arbre : la brique commune": the root is the last
+// verified token and the mask encodes the tree.
+//
+// Design (gfx950):
+//  * split-K over the key axis: block (split s, unit u = b*Hkv + g) streams its
+//    key range once for all R = G*T grouped rows that share KV head g, keeps an
+//    online softmax per row and writes an unnormalised partial (o, m, l);
+//    attn_combine merges the splits with a log-sum-exp;
+//  * the tree mask is the ancestor-or-self bitmask of each query position,
+//    one u64 per row held in registers: key ctx + t is visible to row i iff
+//    bit t of mask(i) is set; prefix keys are visible to every row;
+//  * R < 16 (or fp32 inputs): VALU kernel, 16-byte loads, one key row spread
+//    over D*sizeof/16 lanes, scores reduced across those lanes;
+//  * bf16 with R >= 16: MFMA kernel (v_mfma_f32_16x16x32_bf16).  Scores are
+//    computed transposed, S^T = K Q^T, and the output as O^T += V^T P^T, so the
+//    probabilities produced by the first product are already in the operand
+//    layout of the second: no cross-lane shuffle of P.  K is staged in LDS
+//    row-major, V transposed (key-contiguous, in the key order of P's layout).
+//
+// Scores are kept in the log2 domain (scale * log2(e) folded in) and
+// exponentiated with the hardware exp2.
+
+#include "common.h"
+
+namespace sv {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+struct AttnArgs {
+  const void* q;           // [B, T, Hq, D]
+  const void* k;           // [B, Hkv, L, D]
+  const void* v;           // [B, Hkv, L, D]
+  const int32_t* parents;  // [B, T] or nullptr (chain)
+  float* out;              // [B, T, Hq, D]
+  float* part_o;           // [units, S, R, D]  unnormalised partial outputs
+  float* part_ml;          // [units, S, R, 2]  (running max in log2 units, sum)
+  int B, T, Hq, Hkv, G, D, ctx, L, R, S, chunk;
+  float scale_log2;        // softmax scale * log2(e)
+};
+
+// Ancestor-or-self masks of the T query positions of sequence b, into LDS.
+// Each position walks up its parents (a chain needs no walk).  A parent that
+// is not strictly smaller than its child ends the walk, so malformed input
+// cannot loop or index out of range.
+__device__ __forceinline__ void build_masks(const AttnArgs& a, int b, int* par,
+                                            uint64_t* masks) {
+  const int t = threadIdx.x;
+  if (a.parents != nullptr && t < a.T) par[t] = a.parents[(size_t)b * a.T + t];
+  __syncthreads();
+  if (t < a.T) {
+    uint64_t m;
+    if (a.parents == nullptr) {
+      m = (t == 63) ? ~0ull : ((2ull << t) - 1ull);
+    } else {
+      m = 0;
+      int n = t;
+      while (true) {
+        m |= 1ull << n;
+        const int p = par[n];
+        if (p < 0 || p >= n) break;
+        n = p;
+      }
+    }
+    masks[t] = m;
+  }
+  __syncthreads();
+}
+
+__device__ __forceinline__ bool tail_visible(uint64_t mask, int key, int ctx) {
+  return key < ctx || ((mask >> (key - ctx)) & 1ull);
+}
+
+// Merge two online-softmax states (m in log2 units).
+__device__ __forceinline__ void merge_state(float& m, float& l, float m2, float l2,
+                                            float* o, const float* o2, int n) {
+  const float mx = fmaxf(m, m2);
+  if (mx == kNegInf) return;
+  const float a1 = fast_exp2(m - mx), a2 = fast_exp2(m2 - mx);
+  l = l * a1 + l2 * a2;
+  for (int e = 0; e < n; ++e) o[e] = o[e] * a1 + o2[e] * a2;
+  m = mx;
+}
+
+// ---------------------------------------------------------------------------
+// VALU kernel: 4 waves; grid (S, B*Hkv, ceil(R / RMAX)).
+// ---------------------------------------------------------------------------
+template <typename TIn, int D, int RMAX>
+__global__ __launch_bounds__(256) void attn_valu_kernel(AttnArgs a) {
+  constexpr int EPL = 16 / (int)sizeof(TIn);  // elements per lane per 16-byte load
+  constexpr int LPK = D / EPL;                // lanes sharing one key row
+  constexpr int KPS = kWave / LPK;            // keys per wave step
+  constexpr int U = 4;                        // key steps per iteration
+  static_assert(LPK >= 1 && LPK <= 64 && (64 % LPK) == 0, "layout");
+
+  __shared__ int par[64];
+  __shared__ uint64_t masks[64];
+  __shared__ float red_o[4][RMAX][D];
+  __shared__ float red_ml[4][RMAX][2];
+
+  const int s = blockIdx.x, u = blockIdx.y, rc = blockIdx.z;
+  const int b = u / a.Hkv, g = u % a.Hkv;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int ks = lane / LPK, dp = lane % LPK;
+  const int r0 = rc * RMAX;
+  const int nr = min(RMAX, a.R - r0);
+
+  build_masks(a, b, par, masks);
+
+  float qr[RMAX][EPL];
+  uint64_t mrow[RMAX];
+#pragma unroll
+  for (int r = 0; r < RMAX; ++r) {
+    mrow[r] = 0;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) qr[r][e] = 0.f;
+    if (r < nr) {
+      const int row = r0 + r, t = row / a.G, h = g * a.G + row % a.G;
+      const TIn* qp = (const TIn*)a.q + (((size_t)b * a.T + t) * a.Hq + h) * D + dp * EPL;
+      const u32x4_t w = *(const u32x4_t*)qp;
+      if constexpr (sizeof(TIn) == 2) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          qr[r][2 * e] = bf16_lo(w[e]) * a.scale_log2;
+          qr[r][2 * e + 1] = bf16_hi(w[e]) * a.scale_log2;
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) qr[r][e] = __uint_as_float(w[e]) * a.scale_log2;
+      }
+      mrow[r] = masks[t];
+    }
+  }
+
+  // This block's keys, cut into 4 contiguous per-wave ranges.
+  const int kb = s * a.chunk, ke = min(a.L, kb + a.chunk);
+  const int per = ((ke - kb + 3) / 4 + KPS * U - 1) / (KPS * U) * (KPS * U);
+  const int wb = kb + wave * per, we = min(ke, wb + per);
+
+  float m[RMAX], l[RMAX], o[RMAX][EPL];
+#pragma unroll
+  for (int r = 0; r < RMAX; ++r) {
+    m[r] = kNegInf;
+    l[r] = 0.f;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) o[r][e] = 0.f;
+  }
+
+  const size_t unit_off = (size_t)u * a.L * D;
+  const TIn* kp = (const TIn*)a.k + unit_off;
+  const TIn* vp = (const TIn*)a.v + unit_off;
+
+  for (int key0 = wb; key0 < we; key0 += KPS * U) {
+    float kv[U][EPL], vv[U][EPL];
+    int keyj[U];
+#pragma unroll
+    for (int j = 0; j < U; ++j) {
+      keyj[j] = key0 + j * KPS + ks;
+      u32x4_t wk = {0, 0, 0, 0}, wv = {0, 0, 0, 0};
+      if (keyj[j] < we) {
+        wk = *(const u32x4_t*)(kp + (size_t)keyj[j] * D + dp * EPL);
+        wv = *(const u32x4_t*)(vp + (size_t)keyj[j] * D + dp * EPL);
+      }
+      if constexpr (sizeof(TIn) == 2) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          kv[j][2 * e] = bf16_lo(wk[e]); kv[j][2 * e + 1] = bf16_hi(wk[e]);
+          vv[j][2 * e] = bf16_lo(wv[e]); vv[j][2 * e + 1] = bf16_hi(wv[e]);
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          kv[j][e] = __uint_as_float(wk[e]);
+          vv[j][e] = __uint_as_float(wv[e]);
+        }
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < RMAX; ++r) {
+      if (r >= nr) break;
+      float sc[U];
+#pragma unroll
+      for (int j = 0; j < U; ++j) {
+        float acc = 0.f;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) acc = fmaf(qr[r][e], kv[j][e], acc);
+#pragma unroll
+        for (int off = 1; off < LPK; off <<= 1) acc += __shfl_xor(acc, off);
+        const bool ok = keyj[j] < we && tail_visible(mrow[r], keyj[j], a.ctx);
+        sc[j] = ok ? acc : kNegInf;
+      }
+      float mt = sc[0];
+#pragma unroll
+      for (int j = 1; j < U; ++j) mt = fmaxf(mt, sc[j]);
+      const float mn = fmaxf(m[r], mt);
+      if (mn != kNegInf) {
+        const float alpha = fast_exp2(m[r] - mn);
+        l[r] *= alpha;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) o[r][e] *= alpha;
+#pragma unroll
+        for (int j = 0; j < U; ++j) {
+          const float p = fast_exp2(sc[j] - mn);
+          l[r] += p;
+#pragma unroll
+          for (int e = 0; e < EPL; ++e) o[r][e] = fmaf(p, vv[j][e], o[r][e]);
+        }
+        m[r] = mn;
+      }
+    }
+  }
+
+  // Merge the KPS key slots of the wave (lanes with equal dp hold equal d's).
+#pragma unroll
+  for (int off = LPK; off < kWave; off <<= 1) {
+#pragma unroll
+    for (int r = 0; r < RMAX; ++r) {
+      const float m2 = __shfl_xor(m[r], off), l2 = __shfl_xor(l[r], off);
+      float o2[EPL];
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) o2[e] = __shfl_xor(o[r][e], off);
+      merge_state(m[r], l[r], m2, l2, o[r], o2, EPL);
+    }
+  }
+  // Merge the four waves through LDS.
+  if (ks == 0) {
+#pragma unroll
+    for (int r = 0; r < RMAX; ++r) {
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) red_o[wave][r][dp * EPL + e] = o[r][e];
+      if (dp == 0) { red_ml[wave][r][0] = m[r]; red_ml[wave][r][1] = l[r]; }
+    }
+  }
+  __syncthreads();
+  for (int idx = threadIdx.x; idx < nr * D; idx += 256) {
+    const int r = idx / D, d = idx % D;
+    float mm = red_ml[0][r][0], ll = red_ml[0][r][1], oo = red_o[0][r][d];
+    for (int w = 1; w < 4; ++w) merge_state(mm, ll, red_ml[w][r][0], red_ml[w][r][1], &oo,
+                                            &red_o[w][r][d], 1);
+    const size_t prow = ((size_t)u * a.S + s) * a.R + (r0 + r);
+    a.part_o[prow * D + d] = oo;
+    if (d == 0) { a.part_ml[prow * 2] = mm; a.part_ml[prow * 2 + 1] = ll; }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// MFMA kernel (bf16): W waves x RT row tiles of 16 rows; grid (S, B*Hkv, row chunks).
+// ---------------------------------------------------------------------------
+constexpr int kMfmaKeys = 32;  // keys per tile (the K dimension of the P.V product)
+
+// Position of key k (0..31) of a tile in the contraction order of P.V: lane
+// group g holds keys {4g..4g+3} and {16+4g..16+4g+3} of the tile.
+__device__ __forceinline__ int pv_pos(int k) {
+  return 8 * ((k & 15) >> 2) + 4 * (k >> 4) + (k & 3);
+}
+
+template <int D, int RT, int W>
+__global__ __launch_bounds__(64 * W) void attn_mfma_kernel(AttnArgs a) {
+  constexpr int KT = kMfmaKeys;
+  constexpr int KSTR = D + 8;        // bf16 elements per K row in LDS
+  constexpr int VSTR = KT + 8;       // bf16 elements per transposed V row in LDS
+  constexpr int DT = D / 16;         // 16-wide d tiles of the output
+  constexpr int KK = D / 32;         // 32-deep steps of the score product
+  constexpr int CPR = D / 8;         // 16-byte chunks per key row
+  constexpr int NCH = KT * CPR;      // chunks per tile and tensor
+  constexpr int NPT = (NCH + 64 * W - 1) / (64 * W);
+
+  __shared__ __attribute__((aligned(16))) uint16_t Ks[KT * KSTR];
+  __shared__ __attribute__((aligned(16))) uint16_t Vt[D * VSTR];
+  __shared__ int par[64];
+  __shared__ uint64_t masks[64];
+
+  const int s = blockIdx.x, u = blockIdx.y, rc = blockIdx.z;
+  const int b = u / a.Hkv, gk = u % a.Hkv;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int l16 = lane & 15, g4 = lane >> 4;
+  const int tile0 = (rc * W + wave) * RT;
+
+  build_masks(a, b, par, masks);
+
+  // Q^T operands (B operand of S^T = K Q^T): lane holds Q[row][32kk + 8g4 .. +8].
+  bf16x8_t qf[RT][KK];
+  uint64_t mrow[RT];
+  bool live[RT];
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) {
+    const int row = (tile0 + rt) * 16 + l16;
+    live[rt] = (tile0 + rt) * 16 < a.R;
+    mrow[rt] = 0;
+    u32x4_t z = {0, 0, 0, 0};
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) qf[rt][kk] = __builtin_bit_cast(bf16x8_t, z);
+    if (row < a.R) {
+      const int t = row / a.G, h = gk * a.G + row % a.G;
+      const uint16_t* qp = (const uint16_t*)a.q + (((size_t)b * a.T + t) * a.Hq + h) * D;
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk)
+        qf[rt][kk] = __builtin_bit_cast(bf16x8_t, *(const u32x4_t*)(qp + 32 * kk + 8 * g4));
+      mrow[rt] = masks[t];
+    }
+  }
+
+  f32x4_t acc[RT][DT];
+  float m[RT], lpart[RT];
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) {
+    m[rt] = kNegInf;
+    lpart[rt] = 0.f;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) acc[rt][dt] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+  }
+
+  const int kb = s * a.chunk, ke = min(a.L, kb + a.chunk);
+  const size_t unit_off = (size_t)u * a.L * D;
+  const uint16_t* kg = (const uint16_t*)a.k + unit_off;
+  const uint16_t* vg = (const uint16_t*)a.v + unit_off;
+
+  // Register staging of one tile: K chunks are read row-major (16 lanes per
+  // key row), V chunks key-fastest (32 consecutive keys per column chunk) so
+  // that neighbouring lanes hold neighbouring keys for the transposed store.
+  u32x4_t kreg[NPT], vreg[NPT];
+  auto load_tile = [&](int base) {
+#pragma unroll
+    for (int i = 0; i < NPT; ++i) {
+      const int c = i * 64 * W + tid;
+      u32x4_t zk = {0, 0, 0, 0}, zv = {0, 0, 0, 0};
+      if (c < NCH) {
+        const int kr = c / CPR, kc = c % CPR;
+        if (base + kr < ke) zk = *(const u32x4_t*)(kg + (size_t)(base + kr) * D + 8 * kc);
+        const int vr = c % KT, vc = c / KT;
+        if (base + vr < ke) zv = *(const u32x4_t*)(vg + (size_t)(base + vr) * D + 8 * vc);
+      }
+      kreg[i] = zk;
+      vreg[i] = zv;
+    }
+  };
+  auto store_tile = [&]() {
+#pragma unroll
+    for (int i = 0; i < NPT; ++i) {
+      const int c = i * 64 * W + tid;
+      if (c < NCH) {
+        const int kr = c / CPR, kc = c % CPR;
+        *(u32x4_t*)(Ks + kr * KSTR + 8 * kc) = kreg[i];
+        // Transposed V: neighbouring lanes (keys vr, vr^1) trade halves so each
+        // writes whole dwords holding the pair (V[even][d], V[odd][d]).
+        const int vr = c % KT, vc = c / KT;
+        const bool odd = vr & 1;
+        const uint32_t x0 = odd ? vreg[i][0] : vreg[i][2];
+        const uint32_t x1 = odd ? vreg[i][1] : vreg[i][3];
+        const uint32_t y0 = __shfl_xor(x0, 1), y1 = __shfl_xor(x1, 1);
+        uint32_t* dst = (uint32_t*)(Vt + pv_pos(vr & ~1));
+        if (!odd) {
+          // d = 8vc + 0..3: low half own key, high half the odd neighbour
+          const uint32_t w0 = vreg[i][0], w1 = vreg[i][1];
+          dst[(8 * vc + 0) * (VSTR / 2)] = (w0 & 0xffffu) | (y0 << 16);
+          dst[(8 * vc + 1) * (VSTR / 2)] = (w0 >> 16) | (y0 & 0xffff0000u);
+          dst[(8 * vc + 2) * (VSTR / 2)] = (w1 & 0xffffu) | (y1 << 16);
+          dst[(8 * vc + 3) * (VSTR / 2)] = (w1 >> 16) | (y1 & 0xffff0000u);
+        } else {
+          // d = 8vc + 4..7: low half the even neighbour, high half own key
+          const uint32_t w2 = vreg[i][2], w3 = vreg[i][3];
+          dst[(8 * vc + 4) * (VSTR / 2)] = (y0 & 0xffffu) | (w2 << 16);
+          dst[(8 * vc + 5) * (VSTR / 2)] = (y0 >> 16) | (w2 & 0xffff0000u);
+          dst[(8 * vc + 6) * (VSTR / 2)] = (y1 & 0xffffu) | (w3 << 16);
+          dst[(8 * vc + 7) * (VSTR / 2)] = (y1 >> 16) | (w3 & 0xffff0000u);
+        }
+      }
+    }
+  };
+
+  if (kb < ke) load_tile(kb);
+  for (int base = kb; base < ke; base += KT) {
+    __syncthreads();            // previous tile fully consumed
+    store_tile();
+    __syncthreads();
+    if (base + KT < ke) load_tile(base + KT);   // next tile in flight during compute
+
+    // S^T[key][row] for the tile's two 16-key halves.
+    f32x4_t st[RT][2];
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) st[rt][0] = st[rt][1] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int sub = 0; sub < 2; ++sub) {
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk) {
+        const bf16x8_t kf = __builtin_bit_cast(
+            bf16x8_t, *(const u32x4_t*)(Ks + (16 * sub + l16) * KSTR + 32 * kk + 8 * g4));
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt)
+          if (live[rt])
+            st[rt][sub] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[rt][kk], st[rt][sub],
+                                                                 0, 0, 0);
+      }
+    }
+
+    // Online softmax; lane holds row l16's scores for keys 16sub + 4g4 + r.
+    bf16x8_t pf[RT];
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+      if (!live[rt]) continue;
+      float sc[8];
+#pragma unroll
+      for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int key = base + 16 * sub + 4 * g4 + r;
+          const bool ok = key < ke && tail_visible(mrow[rt], key, a.ctx);
+          sc[4 * sub + r] = ok ? st[rt][sub][r] * a.scale_log2 : kNegInf;
+        }
+      float mt = sc[0];
+#pragma unroll
+      for (int e = 1; e < 8; ++e) mt = fmaxf(mt, sc[e]);
+      mt = fmaxf(mt, __shfl_xor(mt, 16));
+      mt = fmaxf(mt, __shfl_xor(mt, 32));
+      const float mn = fmaxf(m[rt], mt);
+      const float msafe = (mn == kNegInf) ? 0.f : mn;
+      const float alpha = fast_exp2(m[rt] - msafe);
+      m[rt] = mn;
+      float ps = 0.f;
+      uint32_t pk[4];
+#pragma unroll
+      for (int e = 0; e < 8; e += 2) {
+        const float p0 = fast_exp2(sc[e] - msafe), p1 = fast_exp2(sc[e + 1] - msafe);
+        ps += p0 + p1;
+        pk[e / 2] = f32_to_bf16_bits(p0) | (f32_to_bf16_bits(p1) << 16);
+      }
+      lpart[rt] = lpart[rt] * alpha + ps;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) acc[rt][dt] *= alpha;
+      const u32x4_t pw = {pk[0], pk[1], pk[2], pk[3]};
+      pf[rt] = __builtin_bit_cast(bf16x8_t, pw);
+    }
+
+    // O^T[d][row] += V^T[d][keys] P^T[keys][row].
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+      const bf16x8_t vf = __builtin_bit_cast(
+          bf16x8_t, *(const u32x4_t*)(Vt + (16 * dt + l16) * VSTR + 8 * g4));
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt)
+        if (live[rt])
+          acc[rt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf[rt], acc[rt][dt], 0, 0, 0);
+    }
+  }
+
+  // Partials: lane holds O^T[16dt + 4g4 + r][row l16].
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) {
+    float lt = lpart[rt];
+    lt += __shfl_xor(lt, 16);
+    lt += __shfl_xor(lt, 32);
+    const int row = (tile0 + rt) * 16 + l16;
+    if (!live[rt] || row >= a.R) continue;
+    const size_t prow = ((size_t)u * a.S + s) * a.R + row;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+      *(f32x4_t*)(a.part_o + prow * D + 16 * dt + 4 * g4) = acc[rt][dt];
+    if (g4 == 0) { a.part_ml[prow * 2] = m[rt]; a.part_ml[prow * 2 + 1] = lt; }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Split combine: block per (row, unit), one thread per d.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(128) void attn_combine_kernel(AttnArgs a) {
+  const int row = blockIdx.x, u = blockIdx.y, d = threadIdx.x;
+  const int b = u / a.Hkv, gk = u % a.Hkv;
+  const int t = row / a.G, h = gk * a.G + row % a.G;
+  const size_t base = (size_t)u * a.S * a.R + row;
+  float mx = kNegInf;
+  for (int s = 0; s < a.S; ++s) mx = fmaxf(mx, a.part_ml[(base + (size_t)s * a.R) * 2]);
+  float num = 0.f, den = 0.f;
+  for (int s = 0; s < a.S; ++s) {
+    const size_t p = base + (size_t)s * a.R;
+    const float ms = a.part_ml[p * 2];
+    if (ms == kNegInf) continue;
+    const float w = fast_exp2(ms - mx);
+    den = fmaf(w, a.part_ml[p * 2 + 1], den);
+    num = fmaf(w, a.part_o[p * a.D + d], num);
+  }
+  a.out[(((size_t)b * a.T + t) * a.Hq + h) * a.D + d] = num / den;
+}
+
+// ---------------------------------------------------------------------------
+// Host-side dispatch.
+// ---------------------------------------------------------------------------
+template <int D, int RT>
+static void launch_mfma_w(const AttnPlan& p, const AttnArgs& a, hipStream_t st, dim3 grid) {
+  switch (p.waves) {
+    case 1: attn_mfma_kernel<D, RT, 1><<<grid, 64, 0, st>>>(a); break;
+    case 2: attn_mfma_kernel<D, RT, 2><<<grid, 128, 0, st>>>(a); break;
+    case 4: attn_mfma_kernel<D, RT, 4><<<grid, 256, 0, st>>>(a); break;
+    default: attn_mfma_kernel<D, RT, 8><<<grid, 512, 0, st>>>(a); break;
+  }
+}
+
+template <int D>
+static void launch_mfma(const AttnPlan& p, const AttnArgs& a, hipStream_t st, dim3 grid) {
+  switch (p.rt) {
+    case 1: launch_mfma_w<D, 1>(p, a, st, grid); break;
+    case 2: launch_mfma_w<D, 2>(p, a, st, grid); break;
+    case 3: launch_mfma_w<D, 3>(p, a, st, grid); break;
+    default: launch_mfma_w<D, 4>(p, a, st, grid); break;
+  }
+}
+
+template <typename TIn, int D>
+static void launch_valu(const AttnPlan& p, const AttnArgs& a, hipStream_t st, dim3 grid) {
+  switch (p.rmax) {
+    case 1: attn_valu_kernel<TIn, D, 1><<<grid, 256, 0, st>>>(a); break;
+    case 2: attn_valu_kernel<TIn, D, 2><<<grid, 256, 0, st>>>(a); break;
+    case 4: attn_valu_kernel<TIn, D, 4><<<grid, 256, 0, st>>>(a); break;
+    default: attn_valu_kernel<TIn, D, 8><<<grid, 256, 0, st>>>(a); break;
+  }
+}
+
+// Splits and tiles for a problem; a pure function of the shape so that the
+// workspace query and the launch always agree.
+AttnPlan plan_attention(int B, int T, int Hq, int Hkv, int D, int ctx, int bf16) {
+  AttnPlan p{};
+  const int G = Hq / Hkv, R = G * T, L = ctx + T, units = B * Hkv;
+  p.rows = R;
+  p.mfma = bf16 && R >= 16;
+  int tile, blocks_target;
+  if (p.mfma) {
+    const int tiles = (R + 15) / 16;
+    // waves per block from {1, 2, 4, 8}; row tiles per wave 1..4, least padding
+    int best_w = 8, best_rt = 4, best_waste = 1 << 30;
+    for (int w : {1, 2, 4, 8})
+      for (int rt = 1; rt <= 4; ++rt) {
+        const int slots = w * rt;
+        const int chunks = (tiles + slots - 1) / slots;
+        const int waste = chunks * slots - tiles + (chunks - 1) * 64;
+        if (waste < best_waste) { best_waste = waste; best_w = w; best_rt = rt; }
+      }
+    p.waves = best_w;
+    p.rt = best_rt;
+    p.row_chunks = (tiles + best_w * best_rt - 1) / (best_w * best_rt);
+    tile = kMfmaKeys;
+    blocks_target = 2048 / p.waves;
+  } else {
+    const int rr = R < 8 ? R : 8;
+    p.rmax = rr <= 1 ? 1 : rr <= 2 ? 2 : rr <= 4 ? 4 : 8;
+    p.waves = 4;
+    p.row_chunks = (R + p.rmax - 1) / p.rmax;
+    tile = 64;
+    blocks_target = 512;
+  }
+  const int min_chunk = 256;
+  int S = (blocks_target + units * p.row_chunks - 1) / (units * p.row_chunks);
+  const int s_max = (L + min_chunk - 1) / min_chunk;
+  if (S > s_max) S = s_max;
+  if (S < 1) S = 1;
+  int chunk = (L + S - 1) / S;
+  chunk = (chunk + tile - 1) / tile * tile;
+  S = (L + chunk - 1) / chunk;
+  p.splits = S;
+  p.chunk = chunk;
+  p.part_o_bytes = align256((size_t)units * S * R * D * sizeof(float));
+  p.part_ml_bytes = align256((size_t)units * S * R * 2 * sizeof(float));
+  p.total_bytes = p.part_o_bytes + p.part_ml_bytes;
+  return p;
+}
+
+hipError_t launch_attention(const AttnPlan& p, const void* q, const void* k, const void* v,
+                            const int32_t* parents, float* out, int B, int T, int Hq, int Hkv,
+                            int D, int ctx, int bf16, float scale, void* workspace,
+                            hipStream_t st) {
+  AttnArgs a;
+  a.q = q; a.k = k; a.v = v; a.parents = parents; a.out = out;
+  a.part_o = (float*)workspace;
+  a.part_ml = (float*)((char*)workspace + p.part_o_bytes);
+  a.B = B; a.T = T; a.Hq = Hq; a.Hkv = Hkv; a.G = Hq / Hkv; a.D = D; a.ctx = ctx;
+  a.L = ctx + T; a.R = p.rows; a.S = p.splits; a.chunk = p.chunk;
+  a.scale_log2 = scale * kLog2e;
+  const dim3 grid(p.splits, B * Hkv, p.row_chunks);
+  if (p.mfma) {
+    if (D == 64) launch_mfma<64>(p, a, st, grid);
+    else launch_mfma<128>(p, a, st, grid);
+  } else if (bf16) {
+    if (D == 64) launch_valu<uint16_t, 64>(p, a, st, grid);
+    else launch_valu<uint16_t, 128>(p, a, st, grid);
+  } else {
+    if (D == 64) launch_valu<float, 64>(p, a, st, grid);
+    else launch_valu<float, 128>(p, a, st, grid);
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  attn_combine_kernel<<<dim3(p.rows, B * Hkv), D, 0, st>>>(a);
+  return hipGetLastError();
+}
+
+}  // namespace sv

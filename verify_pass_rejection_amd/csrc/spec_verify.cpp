@@ -1,0 +1,138 @@
+// C ABI of the verify step: argument validation, launch plans and dispatch.
+// Every check happens on the host before anything is enqueued.
+
+#include "../../include/spec_verify.h"
+
+#include <math.h>
+
+#include "common.h"
+
+namespace sv {
+AttnPlan plan_attention(int B, int T, int Hq, int Hkv, int D, int ctx, int bf16);
+hipError_t launch_attention(const AttnPlan& p, const void* q, const void* k, const void* v,
+                            const int32_t* parents, float* out, int B, int T, int Hq, int Hkv,
+                            int D, int ctx, int bf16, float scale, void* workspace,
+                            hipStream_t st);
+ChainPlan plan_chain(int B, int N, int V);
+hipError_t launch_chain(const ChainPlan& p, const float* target, const float* draft,
+                        const int32_t* tokens, const float* u_acc, const float* u_draw,
+                        float temperature, int32_t* num_acc, int32_t* out, int B, int N, int V,
+                        void* workspace, hipStream_t st);
+TreePlan plan_tree(int B, int T, int V);
+hipError_t launch_tree(const TreePlan& p, const float* logits, const int32_t* tokens,
+                       const int32_t* parents, int32_t* accept_len, int32_t* path,
+                       int32_t* out, int B, int T, int V, void* workspace, hipStream_t st);
+}  // namespace sv
+
+namespace {
+
+spec_status check_attention(int B, int T, int Hq, int Hkv, int D, int ctx, spec_dtype dtype) {
+  if (B < 0 || T < 0 || Hq < 1 || Hkv < 1 || D < 1 || ctx < 0) return SPEC_ERR_SHAPE;
+  if (Hq % Hkv != 0) return SPEC_ERR_SHAPE;
+  if (dtype != SPEC_F32 && dtype != SPEC_BF16) return SPEC_ERR_UNSUPPORTED;
+  if (T > SPEC_MAX_T || (D != 64 && D != 128)) return SPEC_ERR_UNSUPPORTED;
+  // keep every element index of K/V below 2^31 per (sequence, KV head) unit
+  if ((long long)(ctx + T) * D >= (1ll << 31)) return SPEC_ERR_UNSUPPORTED;
+  return SPEC_OK;
+}
+
+spec_status check_chain(int B, int N, int V) {
+  if (B < 0 || N < 0 || V < 1) return SPEC_ERR_SHAPE;
+  if (V > SPEC_MAX_V || N > SPEC_MAX_T - 1) return SPEC_ERR_UNSUPPORTED;
+  return SPEC_OK;
+}
+
+spec_status check_tree(int B, int T, int V) {
+  if (B < 0 || T < 0 || V < 1) return SPEC_ERR_SHAPE;
+  if (V > SPEC_MAX_V || T > SPEC_MAX_T) return SPEC_ERR_UNSUPPORTED;
+  return SPEC_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* spec_status_string(spec_status s) {
+  switch (s) {
+    case SPEC_OK: return "ok";
+    case SPEC_ERR_NULL: return "a required pointer is NULL";
+    case SPEC_ERR_SHAPE: return "a size is negative or inconsistent";
+    case SPEC_ERR_UNSUPPORTED: return "arguments are outside the supported limits";
+    case SPEC_ERR_WORKSPACE: return "workspace is smaller than the queried size";
+    case SPEC_ERR_HIP: return "the HIP runtime reported a launch error";
+  }
+  return "unknown status";
+}
+
+size_t spec_verify_attention_workspace(int B, int T, int Hq, int Hkv, int D, int ctx,
+                                       spec_dtype dtype) {
+  if (check_attention(B, T, Hq, Hkv, D, ctx, dtype) != SPEC_OK || B == 0 || T == 0) return 0;
+  return sv::plan_attention(B, T, Hq, Hkv, D, ctx, dtype == SPEC_BF16).total_bytes;
+}
+
+spec_status spec_verify_attention(const void* q, const void* k, const void* v,
+                                  const int32_t* parents, float* out, int B, int T, int Hq,
+                                  int Hkv, int D, int ctx, spec_dtype dtype, float scale,
+                                  void* workspace, size_t workspace_bytes, void* hip_stream) {
+  const spec_status c = check_attention(B, T, Hq, Hkv, D, ctx, dtype);
+  if (c != SPEC_OK) return c;
+  if (!isfinite(scale)) return SPEC_ERR_SHAPE;
+  if (B == 0 || T == 0) return SPEC_OK;
+  if (!q || !k || !v || !out || !workspace) return SPEC_ERR_NULL;
+  const sv::AttnPlan p = sv::plan_attention(B, T, Hq, Hkv, D, ctx, dtype == SPEC_BF16);
+  if (workspace_bytes < p.total_bytes) return SPEC_ERR_WORKSPACE;
+  const hipError_t e = sv::launch_attention(p, q, k, v, parents, out, B, T, Hq, Hkv, D, ctx,
+                                            dtype == SPEC_BF16, scale, workspace,
+                                            (hipStream_t)hip_stream);
+  return e == hipSuccess ? SPEC_OK : SPEC_ERR_HIP;
+}
+
+size_t spec_accept_chain_workspace(int B, int N, int V) {
+  if (check_chain(B, N, V) != SPEC_OK || B == 0) return 0;
+  return sv::plan_chain(B, N, V).total_bytes;
+}
+
+spec_status spec_accept_chain(const float* target_logits, const float* draft_logits,
+                              const int32_t* draft_tokens, const float* u_accept,
+                              const float* u_draw, float temperature, int32_t* num_accepted,
+                              int32_t* out_tokens, int B, int N, int V, void* workspace,
+                              size_t workspace_bytes, void* hip_stream) {
+  const spec_status c = check_chain(B, N, V);
+  if (c != SPEC_OK) return c;
+  if (!(temperature > 0.f) || !isfinite(temperature)) return SPEC_ERR_SHAPE;
+  if (B == 0) return SPEC_OK;
+  if (!target_logits || !u_draw || !num_accepted || !out_tokens || !workspace)
+    return SPEC_ERR_NULL;
+  if (N > 0 && (!draft_logits || !draft_tokens || !u_accept)) return SPEC_ERR_NULL;
+  const sv::ChainPlan p = sv::plan_chain(B, N, V);
+  if (workspace_bytes < p.total_bytes) return SPEC_ERR_WORKSPACE;
+  const hipError_t e = sv::launch_chain(p, target_logits, draft_logits, draft_tokens, u_accept,
+                                        u_draw, temperature, num_accepted, out_tokens, B, N, V,
+                                        workspace, (hipStream_t)hip_stream);
+  return e == hipSuccess ? SPEC_OK : SPEC_ERR_HIP;
+}
+
+size_t spec_accept_tree_workspace(int B, int T, int V) {
+  if (check_tree(B, T, V) != SPEC_OK || B == 0 || T == 0) return 0;
+  return sv::plan_tree(B, T, V).total_bytes;
+}
+
+spec_status spec_accept_tree(const float* target_logits, const int32_t* tokens,
+                             const int32_t* parents, int32_t* accept_len, int32_t* path,
+                             int32_t* out_tokens, int B, int T, int V, void* workspace,
+                             size_t workspace_bytes, void* hip_stream) {
+  const spec_status c = check_tree(B, T, V);
+  if (c != SPEC_OK) return c;
+  if (B == 0 || T == 0) return SPEC_OK;
+  if (!target_logits || !tokens || !parents || !accept_len || !path || !out_tokens ||
+      !workspace)
+    return SPEC_ERR_NULL;
+  const sv::TreePlan p = sv::plan_tree(B, T, V);
+  if (workspace_bytes < p.total_bytes) return SPEC_ERR_WORKSPACE;
+  const hipError_t e = sv::launch_tree(p, target_logits, tokens, parents, accept_len, path,
+                                       out_tokens, B, T, V, workspace,
+                                       (hipStream_t)hip_stream);
+  return e == hipSuccess ? SPEC_OK : SPEC_ERR_HIP;
+}
+
+}  // extern "C"
