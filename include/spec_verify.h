@@ -88,7 +88,7 @@ const char* spec_status_string(spec_status status);
  *   parents  [B, T] int32 or NULL; tree: parents[b][0] = -1 (node 0 is the
  *            root, the last verified token), parents[b][i] < i
  *   out      [B, T, Hq, D] float32
- *   scale    softmax scale, normally 1/sqrt(D); must be finite
+ *   scale    softmax scale, normally 1/sqrt(D); must be finite and > 0
  *
  * Limits: 1 <= T <= 64, D in {64, 128}, Hkv >= 1, Hq % Hkv == 0, ctx >= 0.
  * ------------------------------------------------------------------------- */

@@ -62,6 +62,8 @@ def test_attention_validation():
     assert attn(D=96) == UNSUP
     assert attn(dtype=7) == UNSUP
     assert attn(scale=float("nan")) == SHAPE
+    assert attn(scale=0.0) == SHAPE
+    assert attn(scale=-0.5) == SHAPE
     assert attn(ws_bytes=16) == WS
     assert attn(B=0, q=None) == OK          # empty problem: nothing launched
     assert attn(T=0, q=None) == OK

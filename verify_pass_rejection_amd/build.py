@@ -22,6 +22,9 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 CFLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
           # never emit packed fp32 arithmetic
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+          # MFMA accumulators in ordinary VGPRs (no AGPR copies around the
+          # online-softmax rescale)
+          "-mllvm", "-amdgpu-mfma-vgpr-form=1",
           "-I", os.path.join(ROOT, "include"), "-Wall", "-Wno-unused-function"]
 
 

@@ -21,8 +21,9 @@
 //  * bf16 with R >= 16: MFMA kernel (v_mfma_f32_16x16x32_bf16).  Scores are
 //    computed transposed, S^T = K Q^T, and the output as O^T += V^T P^T, so the
 //    probabilities produced by the first product are already in the operand
-//    layout of the second: no cross-lane shuffle of P.  K is staged in LDS
-//    row-major, V transposed (key-contiguous, in the key order of P's layout).
+//    layout of the second: no cross-lane shuffle of P.  K and V are staged in
+//    LDS row-major; the V operand, which needs four consecutive keys per lane,
+//    is read with the gfx950 transposing LDS load (ds_read_tr16_b64).
 //
 // Scores are kept in the log2 domain (scale * log2(e) folded in) and
 // exponentiated with the hardware exp2.
@@ -252,41 +253,57 @@ __global__ __launch_bounds__(256) void attn_valu_kernel(AttnArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// MFMA kernel (bf16): W waves x RT row tiles of 16 rows; grid (S, B*Hkv, row chunks).
+// MFMA kernel (bf16): a block of W waves shares each 32-key K/V tile in LDS;
+// wave w owns RT row tiles of 16 grouped rows.  Grid (S, B*Hkv, row chunks).
+//
+// Products per 32-key tile and row tile (v_mfma_f32_16x16x32_bf16):
+//   S^T[key][row]  = K[key][:] . Q[row][:]    A = K fragment (ds_read_b128),
+//                                             B = Q fragment (registers);
+//   O^T[d][row]   += V^T[d][key] . P[row][key] A = V fragment (two
+//                                             ds_read_tr16_b64), B = P (registers).
+// The accumulator layout of S^T (lane l: row l%16, keys 4(l/16)+r of each
+// 16-key half) is the B-operand layout of P when the contraction runs over
+// the tile's keys in the order pv_key(): so P never leaves its lanes.
 // ---------------------------------------------------------------------------
-constexpr int kMfmaKeys = 32;  // keys per tile (the K dimension of the P.V product)
+constexpr int kMfmaKeys = 32;      // keys per tile (the contraction depth of P.V)
+constexpr float kRescaleLog2 = 8.f;  // lazy rescale: keep a stale max until exceeded by 2^8
 
-// Position of key k (0..31) of a tile in the contraction order of P.V: lane
-// group g holds keys {4g..4g+3} and {16+4g..16+4g+3} of the tile.
-__device__ __forceinline__ int pv_pos(int k) {
-  return 8 * ((k & 15) >> 2) + 4 * (k >> 4) + (k & 3);
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
+// Key (0..31) of the tile that contraction position 8g + e (g = lane/16) stands
+// for: positions 0..3 of a lane group are keys 4g..4g+3 (first 16-key half),
+// positions 4..7 are keys 16+4g..16+4g+3 (second half).
+__device__ __forceinline__ int pv_key(int g, int e) {
+  return (e < 4 ? 4 * g + e : 16 + 4 * g + (e - 4));
 }
 
 template <int D, int RT, int W>
 __global__ __launch_bounds__(64 * W) void attn_mfma_kernel(AttnArgs a) {
   constexpr int KT = kMfmaKeys;
-  constexpr int KSTR = D + 8;        // bf16 elements per K row in LDS
-  constexpr int VSTR = KT + 8;       // bf16 elements per transposed V row in LDS
-  constexpr int DT = D / 16;         // 16-wide d tiles of the output
-  constexpr int KK = D / 32;         // 32-deep steps of the score product
+  constexpr int KSTR = D + 8;        // bf16 per K row in LDS (+16 B: conflict-free b128 reads)
+  constexpr int VSTR = D + 16;       // bf16 per V row in LDS (+32 B: conflict-free tr16 reads)
+  constexpr int DT = D / 16;
+  constexpr int KK = D / 32;
   constexpr int CPR = D / 8;         // 16-byte chunks per key row
   constexpr int NCH = KT * CPR;      // chunks per tile and tensor
   constexpr int NPT = (NCH + 64 * W - 1) / (64 * W);
 
   __shared__ __attribute__((aligned(16))) uint16_t Ks[KT * KSTR];
-  __shared__ __attribute__((aligned(16))) uint16_t Vt[D * VSTR];
+  __shared__ __attribute__((aligned(16))) uint16_t Vs[KT * VSTR];
   __shared__ int par[64];
   __shared__ uint64_t masks[64];
 
   const int s = blockIdx.x, u = blockIdx.y, rc = blockIdx.z;
   const int b = u / a.Hkv, gk = u % a.Hkv;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform (scalar)
   const int l16 = lane & 15, g4 = lane >> 4;
   const int tile0 = (rc * W + wave) * RT;
 
   build_masks(a, b, par, masks);
 
-  // Q^T operands (B operand of S^T = K Q^T): lane holds Q[row][32kk + 8g4 .. +8].
   bf16x8_t qf[RT][KK];
   uint64_t mrow[RT];
   bool live[RT];
@@ -295,7 +312,7 @@ __global__ __launch_bounds__(64 * W) void attn_mfma_kernel(AttnArgs a) {
     const int row = (tile0 + rt) * 16 + l16;
     live[rt] = (tile0 + rt) * 16 < a.R;
     mrow[rt] = 0;
-    u32x4_t z = {0, 0, 0, 0};
+    const u32x4_t z = {0, 0, 0, 0};
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) qf[rt][kk] = __builtin_bit_cast(bf16x8_t, z);
     if (row < a.R) {
@@ -322,68 +339,50 @@ __global__ __launch_bounds__(64 * W) void attn_mfma_kernel(AttnArgs a) {
   const size_t unit_off = (size_t)u * a.L * D;
   const uint16_t* kg = (const uint16_t*)a.k + unit_off;
   const uint16_t* vg = (const uint16_t*)a.v + unit_off;
+  const float c = a.scale_log2;
+  const int clean_end = min(a.ctx, ke);   // tiles ending here need no mask
 
-  // Register staging of one tile: K chunks are read row-major (16 lanes per
-  // key row), V chunks key-fastest (32 consecutive keys per column chunk) so
-  // that neighbouring lanes hold neighbouring keys for the transposed store.
+  // Register staging: chunk i*64W + tid of the tile, 16 lanes per key row.
+  // Keys past the end are clamped to the last row (finite data, masked later).
   u32x4_t kreg[NPT], vreg[NPT];
   auto load_tile = [&](int base) {
 #pragma unroll
     for (int i = 0; i < NPT; ++i) {
-      const int c = i * 64 * W + tid;
-      u32x4_t zk = {0, 0, 0, 0}, zv = {0, 0, 0, 0};
-      if (c < NCH) {
-        const int kr = c / CPR, kc = c % CPR;
-        if (base + kr < ke) zk = *(const u32x4_t*)(kg + (size_t)(base + kr) * D + 8 * kc);
-        const int vr = c % KT, vc = c / KT;
-        if (base + vr < ke) zv = *(const u32x4_t*)(vg + (size_t)(base + vr) * D + 8 * vc);
+      const int ch = i * 64 * W + tid;
+      if (NCH % (64 * W) == 0 || (i * W + wave) * 64 < NCH) {   // uniform per wave
+        const int key = min(base + ch / CPR, a.L - 1);
+        const uint32_t off = (uint32_t)(key * D + 8 * (ch % CPR));
+        kreg[i] = *(const u32x4_t*)(kg + off);
+        vreg[i] = *(const u32x4_t*)(vg + off);
       }
-      kreg[i] = zk;
-      vreg[i] = zv;
     }
   };
   auto store_tile = [&]() {
 #pragma unroll
     for (int i = 0; i < NPT; ++i) {
-      const int c = i * 64 * W + tid;
-      if (c < NCH) {
-        const int kr = c / CPR, kc = c % CPR;
+      const int ch = i * 64 * W + tid;
+      if (NCH % (64 * W) == 0 || (i * W + wave) * 64 < NCH) {
+        const int kr = ch / CPR, kc = ch % CPR;
         *(u32x4_t*)(Ks + kr * KSTR + 8 * kc) = kreg[i];
-        // Transposed V: neighbouring lanes (keys vr, vr^1) trade halves so each
-        // writes whole dwords holding the pair (V[even][d], V[odd][d]).
-        const int vr = c % KT, vc = c / KT;
-        const bool odd = vr & 1;
-        const uint32_t x0 = odd ? vreg[i][0] : vreg[i][2];
-        const uint32_t x1 = odd ? vreg[i][1] : vreg[i][3];
-        const uint32_t y0 = __shfl_xor(x0, 1), y1 = __shfl_xor(x1, 1);
-        uint32_t* dst = (uint32_t*)(Vt + pv_pos(vr & ~1));
-        if (!odd) {
-          // d = 8vc + 0..3: low half own key, high half the odd neighbour
-          const uint32_t w0 = vreg[i][0], w1 = vreg[i][1];
-          dst[(8 * vc + 0) * (VSTR / 2)] = (w0 & 0xffffu) | (y0 << 16);
-          dst[(8 * vc + 1) * (VSTR / 2)] = (w0 >> 16) | (y0 & 0xffff0000u);
-          dst[(8 * vc + 2) * (VSTR / 2)] = (w1 & 0xffffu) | (y1 << 16);
-          dst[(8 * vc + 3) * (VSTR / 2)] = (w1 >> 16) | (y1 & 0xffff0000u);
-        } else {
-          // d = 8vc + 4..7: low half the even neighbour, high half own key
-          const uint32_t w2 = vreg[i][2], w3 = vreg[i][3];
-          dst[(8 * vc + 4) * (VSTR / 2)] = (y0 & 0xffffu) | (w2 << 16);
-          dst[(8 * vc + 5) * (VSTR / 2)] = (y0 >> 16) | (w2 & 0xffff0000u);
-          dst[(8 * vc + 6) * (VSTR / 2)] = (y1 & 0xffffu) | (w3 << 16);
-          dst[(8 * vc + 7) * (VSTR / 2)] = (y1 >> 16) | (w3 & 0xffff0000u);
-        }
+        *(u32x4_t*)(Vs + kr * VSTR + 8 * kc) = vreg[i];
       }
     }
   };
 
+  // Transposed-read addresses of this lane for V fragment halves: lane j of a
+  // 16-lane group points at V[key(j/4)][16dt + 4(j%4) .. +4]; the hardware
+  // hands lane i the four keys' values at d = 16dt + i.
+  const int vkey0 = pv_key(g4, l16 >> 2), vkey1 = pv_key(g4, 4 + (l16 >> 2));
+  const int vcol = 4 * (l16 & 3);
+
   if (kb < ke) load_tile(kb);
   for (int base = kb; base < ke; base += KT) {
-    __syncthreads();            // previous tile fully consumed
+    __syncthreads();
     store_tile();
     __syncthreads();
-    if (base + KT < ke) load_tile(base + KT);   // next tile in flight during compute
+    if (base + KT < ke) load_tile(base + KT);
 
-    // S^T[key][row] for the tile's two 16-key halves.
+    // S^T for the tile's two 16-key halves.
     f32x4_t st[RT][2];
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) st[rt][0] = st[rt][1] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
@@ -401,7 +400,8 @@ __global__ __launch_bounds__(64 * W) void attn_mfma_kernel(AttnArgs a) {
       }
     }
 
-    // Online softmax; lane holds row l16's scores for keys 16sub + 4g4 + r.
+    // Online softmax in log2 units with a lazily refreshed reference max.
+    const bool clean = base + KT <= clean_end;
     bf16x8_t pf[RT];
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) {
@@ -410,40 +410,54 @@ __global__ __launch_bounds__(64 * W) void attn_mfma_kernel(AttnArgs a) {
 #pragma unroll
       for (int sub = 0; sub < 2; ++sub)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int key = base + 16 * sub + 4 * g4 + r;
-          const bool ok = key < ke && tail_visible(mrow[rt], key, a.ctx);
-          sc[4 * sub + r] = ok ? st[rt][sub][r] * a.scale_log2 : kNegInf;
+        for (int r = 0; r < 4; ++r) sc[4 * sub + r] = st[rt][sub][r];
+      if (!clean) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int key = base + (e < 4 ? 4 * g4 + e : 16 + 4 * g4 + e - 4);
+          if (!(key < ke && tail_visible(mrow[rt], key, a.ctx))) sc[e] = kNegInf;
         }
+      }
       float mt = sc[0];
 #pragma unroll
       for (int e = 1; e < 8; ++e) mt = fmaxf(mt, sc[e]);
       mt = fmaxf(mt, __shfl_xor(mt, 16));
       mt = fmaxf(mt, __shfl_xor(mt, 32));
-      const float mn = fmaxf(m[rt], mt);
-      const float msafe = (mn == kNegInf) ? 0.f : mn;
-      const float alpha = fast_exp2(m[rt] - msafe);
-      m[rt] = mn;
+      mt *= c;                                  // scale > 0: max commutes with scaling
+      const bool bump = mt > m[rt] + kRescaleLog2;
+      if (__any(bump)) {
+        const float mn = bump ? mt : m[rt];
+        const float alpha = fast_exp2(m[rt] - mn);   // m = -inf: 0
+        m[rt] = mn;
+        lpart[rt] *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) acc[rt][dt] *= alpha;
+      }
+      const float msafe = (m[rt] == kNegInf) ? 0.f : m[rt];
       float ps = 0.f;
-      uint32_t pk[4];
+      bf16x2_t pk[4];
 #pragma unroll
       for (int e = 0; e < 8; e += 2) {
-        const float p0 = fast_exp2(sc[e] - msafe), p1 = fast_exp2(sc[e + 1] - msafe);
+        const float p0 = fast_exp2(fmaf(sc[e], c, -msafe));
+        const float p1 = fast_exp2(fmaf(sc[e + 1], c, -msafe));
         ps += p0 + p1;
-        pk[e / 2] = f32_to_bf16_bits(p0) | (f32_to_bf16_bits(p1) << 16);
+        pk[e / 2] = __builtin_convertvector((f32x2_t){p0, p1}, bf16x2_t);
       }
-      lpart[rt] = lpart[rt] * alpha + ps;
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt) acc[rt][dt] *= alpha;
-      const u32x4_t pw = {pk[0], pk[1], pk[2], pk[3]};
-      pf[rt] = __builtin_bit_cast(bf16x8_t, pw);
+      lpart[rt] += ps;
+      pf[rt] = __builtin_shufflevector(__builtin_shufflevector(pk[0], pk[1], 0, 1, 2, 3),
+                                       __builtin_shufflevector(pk[2], pk[3], 0, 1, 2, 3),
+                                       0, 1, 2, 3, 4, 5, 6, 7);
     }
 
-    // O^T[d][row] += V^T[d][keys] P^T[keys][row].
+    // O^T += V^T P^T.
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
-      const bf16x8_t vf = __builtin_bit_cast(
-          bf16x8_t, *(const u32x4_t*)(Vt + (16 * dt + l16) * VSTR + 8 * g4));
+      const s16x4_t v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) s16x4_t*)(Vs + vkey0 * VSTR + 16 * dt + vcol));
+      const s16x4_t v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) s16x4_t*)(Vs + vkey1 * VSTR + 16 * dt + vcol));
+      const bf16x8_t vf = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(v0, v1, 0, 1, 2, 3,
+                                                                               4, 5, 6, 7));
 #pragma unroll
       for (int rt = 0; rt < RT; ++rt)
         if (live[rt])
@@ -451,7 +465,7 @@ __global__ __launch_bounds__(64 * W) void attn_mfma_kernel(AttnArgs a) {
     }
   }
 
-  // Partials: lane holds O^T[16dt + 4g4 + r][row l16].
+  // Partials: lane holds O^T[16dt + 4g4 + r][row l16] (unnormalised, max m).
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) {
     float lt = lpart[rt];
@@ -497,7 +511,11 @@ static void launch_mfma_w(const AttnPlan& p, const AttnArgs& a, hipStream_t st, 
   switch (p.waves) {
     case 1: attn_mfma_kernel<D, RT, 1><<<grid, 64, 0, st>>>(a); break;
     case 2: attn_mfma_kernel<D, RT, 2><<<grid, 128, 0, st>>>(a); break;
+    case 3: attn_mfma_kernel<D, RT, 3><<<grid, 192, 0, st>>>(a); break;
     case 4: attn_mfma_kernel<D, RT, 4><<<grid, 256, 0, st>>>(a); break;
+    case 5: attn_mfma_kernel<D, RT, 5><<<grid, 320, 0, st>>>(a); break;
+    case 6: attn_mfma_kernel<D, RT, 6><<<grid, 384, 0, st>>>(a); break;
+    case 7: attn_mfma_kernel<D, RT, 7><<<grid, 448, 0, st>>>(a); break;
     default: attn_mfma_kernel<D, RT, 8><<<grid, 512, 0, st>>>(a); break;
   }
 }
@@ -507,8 +525,7 @@ static void launch_mfma(const AttnPlan& p, const AttnArgs& a, hipStream_t st, di
   switch (p.rt) {
     case 1: launch_mfma_w<D, 1>(p, a, st, grid); break;
     case 2: launch_mfma_w<D, 2>(p, a, st, grid); break;
-    case 3: launch_mfma_w<D, 3>(p, a, st, grid); break;
-    default: launch_mfma_w<D, 4>(p, a, st, grid); break;
+    default: launch_mfma_w<D, 3>(p, a, st, grid); break;
   }
 }
 
@@ -532,20 +549,13 @@ AttnPlan plan_attention(int B, int T, int Hq, int Hkv, int D, int ctx, int bf16)
   int tile, blocks_target;
   if (p.mfma) {
     const int tiles = (R + 15) / 16;
-    // waves per block from {1, 2, 4, 8}; row tiles per wave 1..4, least padding
-    int best_w = 8, best_rt = 4, best_waste = 1 << 30;
-    for (int w : {1, 2, 4, 8})
-      for (int rt = 1; rt <= 4; ++rt) {
-        const int slots = w * rt;
-        const int chunks = (tiles + slots - 1) / slots;
-        const int waste = chunks * slots - tiles + (chunks - 1) * 64;
-        if (waste < best_waste) { best_waste = waste; best_w = w; best_rt = rt; }
-      }
-    p.waves = best_w;
-    p.rt = best_rt;
-    p.row_chunks = (tiles + best_w * best_rt - 1) / (best_w * best_rt);
+    // one to three 16-row tiles per wave, at most 8 waves; the rest in row chunks
+    p.rt = tiles <= 8 ? 1 : tiles <= 16 ? 2 : 3;
+    int waves = (tiles + p.rt - 1) / p.rt;
+    p.row_chunks = (waves + 7) / 8;
+    p.waves = (waves + p.row_chunks - 1) / p.row_chunks;
     tile = kMfmaKeys;
-    blocks_target = 2048 / p.waves;
+    blocks_target = 1024;
   } else {
     const int rr = R < 8 ? R : 8;
     p.rmax = rr <= 1 ? 1 : rr <= 2 ? 2 : rr <= 4 ? 4 : 8;

@@ -76,7 +76,7 @@ spec_status spec_verify_attention(const void* q, const void* k, const void* v,
                                   void* workspace, size_t workspace_bytes, void* hip_stream) {
   const spec_status c = check_attention(B, T, Hq, Hkv, D, ctx, dtype);
   if (c != SPEC_OK) return c;
-  if (!isfinite(scale)) return SPEC_ERR_SHAPE;
+  if (!isfinite(scale) || !(scale > 0.f)) return SPEC_ERR_SHAPE;
   if (B == 0 || T == 0) return SPEC_OK;
   if (!q || !k || !v || !out || !workspace) return SPEC_ERR_NULL;
   const sv::AttnPlan p = sv::plan_attention(B, T, Hq, Hkv, D, ctx, dtype == SPEC_BF16);
