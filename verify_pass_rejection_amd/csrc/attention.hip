@@ -80,6 +80,10 @@ __device__ __forceinline__ bool tail_visible(uint64_t mask, int key, int ctx) {
   return key < ctx || ((mask >> (key - ctx)) & 1ull);
 }
 
+// Lazy rescaling: the running reference max is kept until a new score exceeds
+// it by 2^8 (in log2 units); the final ratio is unchanged by the choice.
+constexpr float kRescaleLog2 = 8.f;
+
 // Merge two online-softmax states (m in log2 units).
 __device__ __forceinline__ void merge_state(float& m, float& l, float m2, float l2,
                                             float* o, const float* o2, int n) {
@@ -92,15 +96,41 @@ __device__ __forceinline__ void merge_state(float& m, float& l, float m2, float 
 }
 
 // ---------------------------------------------------------------------------
-// VALU kernel: 4 waves; grid (S, B*Hkv, ceil(R / RMAX)).
+// VALU kernel: 4 independent waves per block; grid (S, B*Hkv, ceil(R / RMAX)).
+// A key row is spread over LPK lanes (one 16-byte load each); bf16 scores use
+// v_dot2_f32_bf16 and are summed across the LPK lanes with a DPP butterfly,
+// which leaves the bit-identical total in every lane of the group.  Each lane
+// group keeps its own online-softmax state over its keys; the groups and the
+// waves are merged at the end.
 // ---------------------------------------------------------------------------
+typedef __bf16 bf16x2v_t __attribute__((ext_vector_type(2)));
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xf, 0xf, false));
+}
+
+// Sum over aligned groups of LPK lanes (LPK in {8, 16, 32}); every lane of a
+// group ends with the same bits (each step adds a commuted pair).
+template <int LPK>
+__device__ __forceinline__ float group_sum(float v) {
+  v += dpp_f<0xB1>(v);     // quad_perm [1,0,3,2]: lane ^ 1
+  v += dpp_f<0x4E>(v);     // quad_perm [2,3,0,1]: lane ^ 2
+  v += dpp_f<0x141>(v);    // row_half_mirror: quad 0 <-> quad 1 of each 8
+  if constexpr (LPK >= 16) v += dpp_f<0x140>(v);   // row_mirror: halves of each 16
+  if constexpr (LPK >= 32) v += __shfl_xor(v, 16);
+  return v;
+}
+
 template <typename TIn, int D, int RMAX>
 __global__ __launch_bounds__(256) void attn_valu_kernel(AttnArgs a) {
+  constexpr bool BF = sizeof(TIn) == 2;
   constexpr int EPL = 16 / (int)sizeof(TIn);  // elements per lane per 16-byte load
   constexpr int LPK = D / EPL;                // lanes sharing one key row
   constexpr int KPS = kWave / LPK;            // keys per wave step
   constexpr int U = 4;                        // key steps per iteration
-  static_assert(LPK >= 1 && LPK <= 64 && (64 % LPK) == 0, "layout");
+  constexpr int KPI = KPS * U;                // keys per wave iteration
+  static_assert(LPK >= 8 && LPK <= 32, "layout");
 
   __shared__ int par[64];
   __shared__ uint64_t masks[64];
@@ -109,42 +139,35 @@ __global__ __launch_bounds__(256) void attn_valu_kernel(AttnArgs a) {
 
   const int s = blockIdx.x, u = blockIdx.y, rc = blockIdx.z;
   const int b = u / a.Hkv, g = u % a.Hkv;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int ks = lane / LPK, dp = lane % LPK;
   const int r0 = rc * RMAX;
   const int nr = min(RMAX, a.R - r0);
 
   build_masks(a, b, par, masks);
 
-  float qr[RMAX][EPL];
+  // Query rows: raw bf16 pairs (dot2 operands) or fp32 values.
+  u32x4_t qw[RMAX];
   uint64_t mrow[RMAX];
 #pragma unroll
   for (int r = 0; r < RMAX; ++r) {
+    qw[r] = (u32x4_t){0, 0, 0, 0};
     mrow[r] = 0;
-#pragma unroll
-    for (int e = 0; e < EPL; ++e) qr[r][e] = 0.f;
     if (r < nr) {
       const int row = r0 + r, t = row / a.G, h = g * a.G + row % a.G;
-      const TIn* qp = (const TIn*)a.q + (((size_t)b * a.T + t) * a.Hq + h) * D + dp * EPL;
-      const u32x4_t w = *(const u32x4_t*)qp;
-      if constexpr (sizeof(TIn) == 2) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          qr[r][2 * e] = bf16_lo(w[e]) * a.scale_log2;
-          qr[r][2 * e + 1] = bf16_hi(w[e]) * a.scale_log2;
-        }
-      } else {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) qr[r][e] = __uint_as_float(w[e]) * a.scale_log2;
-      }
+      qw[r] = *(const u32x4_t*)((const TIn*)a.q + (((size_t)b * a.T + t) * a.Hq + h) * D +
+                                dp * EPL);
       mrow[r] = masks[t];
     }
   }
 
   // This block's keys, cut into 4 contiguous per-wave ranges.
   const int kb = s * a.chunk, ke = min(a.L, kb + a.chunk);
-  const int per = ((ke - kb + 3) / 4 + KPS * U - 1) / (KPS * U) * (KPS * U);
+  const int per = ((ke - kb + 3) / 4 + KPI - 1) / KPI * KPI;
   const int wb = kb + wave * per, we = min(ke, wb + per);
+  const int clean_end = min(a.ctx, we);
+  const float c = a.scale_log2;
 
   float m[RMAX], l[RMAX], o[RMAX][EPL];
 #pragma unroll
@@ -156,34 +179,41 @@ __global__ __launch_bounds__(256) void attn_valu_kernel(AttnArgs a) {
   }
 
   const size_t unit_off = (size_t)u * a.L * D;
-  const TIn* kp = (const TIn*)a.k + unit_off;
-  const TIn* vp = (const TIn*)a.v + unit_off;
+  const TIn* kp = (const TIn*)a.k + unit_off + dp * EPL;
+  const TIn* vp = (const TIn*)a.v + unit_off + dp * EPL;
+  const int last = a.L - 1;
 
-  for (int key0 = wb; key0 < we; key0 += KPS * U) {
-    float kv[U][EPL], vv[U][EPL];
-    int keyj[U];
+  u32x4_t kw[U], vw[U];
+  auto load = [&](int key0) {
 #pragma unroll
     for (int j = 0; j < U; ++j) {
-      keyj[j] = key0 + j * KPS + ks;
-      u32x4_t wk = {0, 0, 0, 0}, wv = {0, 0, 0, 0};
-      if (keyj[j] < we) {
-        wk = *(const u32x4_t*)(kp + (size_t)keyj[j] * D + dp * EPL);
-        wv = *(const u32x4_t*)(vp + (size_t)keyj[j] * D + dp * EPL);
-      }
-      if constexpr (sizeof(TIn) == 2) {
+      const uint32_t off = (uint32_t)(min(key0 + j * KPS + ks, last) * D);
+      kw[j] = *(const u32x4_t*)(kp + off);
+      vw[j] = *(const u32x4_t*)(vp + off);
+    }
+  };
+  if (wb < we) load(wb);
+  for (int key0 = wb; key0 < we; key0 += KPI) {
+    u32x4_t kcur[U], vcur[U];
+#pragma unroll
+    for (int j = 0; j < U; ++j) { kcur[j] = kw[j]; vcur[j] = vw[j]; }
+    if (key0 + KPI < we) load(key0 + KPI);       // next keys in flight
+
+    float vf[U][EPL];
+#pragma unroll
+    for (int j = 0; j < U; ++j) {
+      if constexpr (BF) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          kv[j][2 * e] = bf16_lo(wk[e]); kv[j][2 * e + 1] = bf16_hi(wk[e]);
-          vv[j][2 * e] = bf16_lo(wv[e]); vv[j][2 * e + 1] = bf16_hi(wv[e]);
+          vf[j][2 * e] = bf16_lo(vcur[j][e]);
+          vf[j][2 * e + 1] = bf16_hi(vcur[j][e]);
         }
       } else {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          kv[j][e] = __uint_as_float(wk[e]);
-          vv[j][e] = __uint_as_float(wv[e]);
-        }
+        for (int e = 0; e < 4; ++e) vf[j][e] = __uint_as_float(vcur[j][e]);
       }
     }
+    const bool clean = key0 + KPI <= clean_end;
 #pragma unroll
     for (int r = 0; r < RMAX; ++r) {
       if (r >= nr) break;
@@ -191,30 +221,47 @@ __global__ __launch_bounds__(256) void attn_valu_kernel(AttnArgs a) {
 #pragma unroll
       for (int j = 0; j < U; ++j) {
         float acc = 0.f;
+        if constexpr (BF) {
 #pragma unroll
-        for (int e = 0; e < EPL; ++e) acc = fmaf(qr[r][e], kv[j][e], acc);
+          for (int e = 0; e < 4; ++e) {
+            // copy the vector elements out first: a bit_cast of an ext-vector
+            // element expression reads element 0 whatever the index
+            const uint32_t qe = qw[r][e], ke2 = kcur[j][e];
+            acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2v_t, qe),
+                                                  __builtin_bit_cast(bf16x2v_t, ke2), acc,
+                                                  false);
+          }
+        } else {
 #pragma unroll
-        for (int off = 1; off < LPK; off <<= 1) acc += __shfl_xor(acc, off);
-        const bool ok = keyj[j] < we && tail_visible(mrow[r], keyj[j], a.ctx);
-        sc[j] = ok ? acc : kNegInf;
+          for (int e = 0; e < 4; ++e)
+            acc = fmaf(__uint_as_float(qw[r][e]), __uint_as_float(kcur[j][e]), acc);
+        }
+        sc[j] = group_sum<LPK>(acc);
+        if (!clean) {
+          const int key = key0 + j * KPS + ks;
+          if (!(key < we && tail_visible(mrow[r], key, a.ctx))) sc[j] = kNegInf;
+        }
       }
       float mt = sc[0];
 #pragma unroll
       for (int j = 1; j < U; ++j) mt = fmaxf(mt, sc[j]);
-      const float mn = fmaxf(m[r], mt);
-      if (mn != kNegInf) {
-        const float alpha = fast_exp2(m[r] - mn);
+      mt *= c;
+      const bool bump = mt > m[r] + kRescaleLog2;
+      if (__any(bump)) {
+        // lanes that keep their reference (possibly -inf) must not compute -inf - -inf
+        const float alpha = bump ? fast_exp2(m[r] - mt) : 1.f;
+        if (bump) m[r] = mt;
         l[r] *= alpha;
 #pragma unroll
         for (int e = 0; e < EPL; ++e) o[r][e] *= alpha;
+      }
+      const float msafe = (m[r] == kNegInf) ? 0.f : m[r];
 #pragma unroll
-        for (int j = 0; j < U; ++j) {
-          const float p = fast_exp2(sc[j] - mn);
-          l[r] += p;
+      for (int j = 0; j < U; ++j) {
+        const float p = fast_exp2(fmaf(sc[j], c, -msafe));
+        l[r] += p;
 #pragma unroll
-          for (int e = 0; e < EPL; ++e) o[r][e] = fmaf(p, vv[j][e], o[r][e]);
-        }
-        m[r] = mn;
+        for (int e = 0; e < EPL; ++e) o[r][e] = fmaf(p, vf[j][e], o[r][e]);
       }
     }
   }
@@ -266,7 +313,6 @@ __global__ __launch_bounds__(256) void attn_valu_kernel(AttnArgs a) {
 // the tile's keys in the order pv_key(): so P never leaves its lanes.
 // ---------------------------------------------------------------------------
 constexpr int kMfmaKeys = 32;      // keys per tile (the contraction depth of P.V)
-constexpr float kRescaleLog2 = 8.f;  // lazy rescale: keep a stale max until exceeded by 2^8
 
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
@@ -426,9 +472,9 @@ __global__ __launch_bounds__(64 * W) void attn_mfma_kernel(AttnArgs a) {
       mt *= c;                                  // scale > 0: max commutes with scaling
       const bool bump = mt > m[rt] + kRescaleLog2;
       if (__any(bump)) {
-        const float mn = bump ? mt : m[rt];
-        const float alpha = fast_exp2(m[rt] - mn);   // m = -inf: 0
-        m[rt] = mn;
+        // lanes that keep their reference (possibly -inf) must not compute -inf - -inf
+        const float alpha = bump ? fast_exp2(m[rt] - mt) : 1.f;   // m = -inf: 0
+        if (bump) m[rt] = mt;
         lpart[rt] *= alpha;
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) acc[rt][dt] *= alpha;
@@ -540,7 +586,17 @@ static void launch_valu(const AttnPlan& p, const AttnArgs& a, hipStream_t st, di
 }
 
 // Splits and tiles for a problem; a pure function of the shape so that the
-// workspace query and the launch always agree.
+// workspace query and the launch always agree.  The block targets aim at one
+// full wave of resident blocks on the 256 CUs.
+#ifndef SV_MFMA_BLOCKS
+#define SV_MFMA_BLOCKS 1024
+#endif
+#ifndef SV_VALU_BLOCKS
+#define SV_VALU_BLOCKS 512
+#endif
+#ifndef SV_MIN_CHUNK
+#define SV_MIN_CHUNK 256
+#endif
 AttnPlan plan_attention(int B, int T, int Hq, int Hkv, int D, int ctx, int bf16) {
   AttnPlan p{};
   const int G = Hq / Hkv, R = G * T, L = ctx + T, units = B * Hkv;
@@ -555,16 +611,16 @@ AttnPlan plan_attention(int B, int T, int Hq, int Hkv, int D, int ctx, int bf16)
     p.row_chunks = (waves + 7) / 8;
     p.waves = (waves + p.row_chunks - 1) / p.row_chunks;
     tile = kMfmaKeys;
-    blocks_target = 1024;
+    blocks_target = SV_MFMA_BLOCKS;
   } else {
     const int rr = R < 8 ? R : 8;
     p.rmax = rr <= 1 ? 1 : rr <= 2 ? 2 : rr <= 4 ? 4 : 8;
     p.waves = 4;
     p.row_chunks = (R + p.rmax - 1) / p.rmax;
     tile = 64;
-    blocks_target = 512;
+    blocks_target = SV_VALU_BLOCKS;
   }
-  const int min_chunk = 256;
+  const int min_chunk = SV_MIN_CHUNK;
   int S = (blocks_target + units * p.row_chunks - 1) / (units * p.row_chunks);
   const int s_max = (L + min_chunk - 1) / min_chunk;
   if (S > s_max) S = s_max;
