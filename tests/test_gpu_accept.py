@@ -158,3 +158,21 @@ def test_accept_deterministic_run_twice():
     b = nat.spec_accept_chain(d["target_logits"], d["draft_logits"], d["draft_tokens"],
                               d["u_accept"], d["u_draw"])
     assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+
+
+def test_chain_fallbacks_across_draw_chunks():
+    """Several vocabulary chunks per row: the empty-residual fallback to p,
+    residual mass that sits only in a late chunk, and ordinary rows."""
+    dev = device()
+    w = I.WORKLOADS["large_batch_chain"].with_(B=48, T=4, V=20000, seed=41)
+    d = I.make_chain_inputs(w, dev)
+    # identical rows and an invalid first draft: rejected with an empty residual
+    d["draft_logits"][0:16] = d["target_logits"][0:16, :w.N]
+    d["draft_tokens"][0:16, 0] = -1
+    # target concentrated on token 17000 (a late chunk), draft elsewhere: the
+    # residual at the first rejection is that token alone
+    d["target_logits"][16:32] = -float("inf")
+    d["target_logits"][16:32, :, 17000] = 0.0
+    num, out, _ = compare_chain(d, label="chunked fallbacks")
+    assert np.all(num[0:16] == 0)
+    assert np.all(out[16:32][np.arange(16), num[16:32]] == 17000)

@@ -7,16 +7,21 @@
 // pure target sampling.  The pass gives N+1 target distributions, so when all
 // N drafts are kept the last one supplies a bonus token.
 //
-// Two kernels:
+// Four kernels (kernel boundaries order every step; no in-kernel signalling):
 //  chain_stats  — one pass over every logit row (all B*(2N+1) rows), per chunk
 //                 the row maximum and sum of 2^((z - max) log2(e)/tau);
-//  chain_draw   — one block per sequence: merges the chunk statistics into
-//                 each row's normaliser, runs the N ratio tests (two gathers a
-//                 row), takes the first rejection k, then draws the committed
-//                 token from row k only (the residual (p_k - q_k)+, or p_N):
-//                 a first sweep computes chunk sums of the weights, a second
-//                 re-scans the one chunk holding the crossing.  Only the drawn
-//                 row pair is read a second time.
+//  chain_decide — one block per sequence: merges the chunk statistics into
+//                 the row normalisers, runs the N ratio tests (two gathers a
+//                 row), takes the first rejection k and records the normalisers
+//                 of the row(s) to draw from;
+//  chain_chunks — grid (vocabulary chunk, sequence): every block sums the
+//                 weights of its chunk of the drawn row (the residual
+//                 (p_k - q_k)+, or p_N);
+//  chain_select — one block per sequence: locates the chunk holding the
+//                 inverse-CDF crossing from the chunk sums and re-scans that
+//                 one chunk (if the residual is empty it first sums p_k's
+//                 chunks itself).  Only the drawn row pair is read a second
+//                 time.
 //
 // Every row's ratio test depends on that row alone, so computing all of them
 // and then taking the first rejection gives the same result as the
@@ -35,16 +40,24 @@ struct ChainArgs {
   int32_t* num_acc;      // [B]
   int32_t* out;          // [B, N+1]
   float2* stats;         // [B, 2N+1, nchunks]: (row max, sum of 2^((z-max)c))
-  int B, N, V, chunk, nchunks;
+  float* csum;           // [B, 2, dchunks]: chunk sums of the residual and of p
+  float4* decision;      // [B]: (k, p-row max, p-row log2 sum, unused) ...
+  float4* decision_q;    // [B]: (q-row max, q-row log2 sum, unused, unused)
+  int B, N, V, chunk, nchunks, dchunks;
   float c2;              // log2(e) / temperature
 };
 
-constexpr int kStatsThreads = 256;
-constexpr int kStatsChunk = 8192;     // logits per stats block
+#ifndef SV_STATS_THREADS
+#define SV_STATS_THREADS 256
+#endif
+#ifndef SV_STATS_CHUNK
+#define SV_STATS_CHUNK 8192
+#endif
+constexpr int kStatsThreads = SV_STATS_THREADS;
+constexpr int kStatsChunk = SV_STATS_CHUNK;   // logits per stats block
 constexpr int kDrawThreads = 1024;
 constexpr int kDrawPer = 4;           // weights per thread per draw chunk
 constexpr int kDrawChunk = kDrawThreads * kDrawPer;
-constexpr int kMaxDrawChunks = (1 << 24) / kDrawChunk;
 
 __device__ __forceinline__ const float* chain_row(const ChainArgs& a, int b, int rho) {
   return rho <= a.N ? a.target + ((size_t)b * (a.N + 1) + rho) * a.V
@@ -176,116 +189,151 @@ __device__ __forceinline__ void chunk_scan(const float* w, float* prefix, float*
   for (int e = 0; e < kDrawPer; ++e) prefix[e] = off + local[e];
 }
 
-template <int VEC>
-__global__ __launch_bounds__(kDrawThreads) void chain_draw_kernel(ChainArgs a) {
+__global__ __launch_bounds__(256) void chain_decide_kernel(ChainArgs a) {
   __shared__ float row_m[128], row_l[128];     // per row: max, log2(sum)
-  __shared__ float ratio_ok[64];
-  __shared__ float csum[kMaxDrawChunks];
-  __shared__ float wave_tot[kDrawThreads / kWave], wave_off[kDrawThreads / kWave];
-  __shared__ int wave_hit[kDrawThreads / kWave];
-  __shared__ int s_k, s_chunk, s_y;
-  __shared__ float s_carry, s_target;
-  __shared__ int s_mode;
-
+  __shared__ int keep[64];
   const int b = blockIdx.x, tid = threadIdx.x;
   const int N = a.N, rows = 2 * N + 1;
   const int lane = tid & 63, wave = tid >> 6;
 
-  // 1. Row normalisers from the chunk statistics (fixed chunk order).
-  if (tid < rows) {
-    const float2* st = a.stats + ((size_t)b * rows + tid) * a.nchunks;
-    float M = st[0].x, S = st[0].y;
-    for (int c = 1; c < a.nchunks; ++c) merge_ms(M, S, st[c].x, st[c].y, a.c2);
-    row_m[tid] = M;
-    row_l[tid] = log2f(S);
+  // Row normalisers: one wave per row merges the row's chunk statistics in a
+  // fixed tree order (lane-strided partial merges, then a butterfly).
+  for (int r = wave; r < rows; r += 4) {
+    const float2* st = a.stats + ((size_t)b * rows + r) * a.nchunks;
+    float M = kNegInf, S = 0.f;
+    for (int i = lane; i < a.nchunks; i += kWave) merge_ms(M, S, st[i].x, st[i].y, a.c2);
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) {
+      const float m2 = __shfl_xor(M, off), s2 = __shfl_xor(S, off);
+      merge_ms(M, S, m2, s2, a.c2);
+    }
+    if (lane == 0) { row_m[r] = M; row_l[r] = log2f(S); }
   }
   __syncthreads();
 
-  // 2. Ratio tests: keep x_i iff u < p_i(x_i)/q_i(x_i).
+  // Ratio tests: keep x_i iff u < p_i(x_i)/q_i(x_i).
   if (tid < N) {
     const int x = a.tokens[(size_t)b * N + tid];
-    bool keep = false;
+    bool ok = false;
     if (x >= 0 && x < a.V) {
       const float zp = a.target[((size_t)b * (N + 1) + tid) * a.V + x];
       const float zq = a.draft[((size_t)b * N + tid) * a.V + x];
       const float lp = (zp - row_m[tid]) * a.c2 - row_l[tid];
       const float lq = (zq - row_m[N + 1 + tid]) * a.c2 - row_l[N + 1 + tid];
       const float r = exp2f(lp - lq);   // q = 0: +inf when p > 0; NaN (reject) when both 0
-      keep = a.u_acc[(size_t)b * N + tid] < r;
+      ok = a.u_acc[(size_t)b * N + tid] < r;
     }
-    ratio_ok[tid] = keep ? 1.f : 0.f;
+    keep[tid] = ok;
   }
   __syncthreads();
   if (tid == 0) {
     int k = N;
     for (int i = 0; i < N; ++i)
-      if (ratio_ok[i] == 0.f) { k = i; break; }
-    s_k = k;
-    s_mode = k < N ? 1 : 0;
+      if (!keep[i]) { k = i; break; }
+    const float mq = k < N ? row_m[N + 1 + k] : 0.f, lq = k < N ? row_l[N + 1 + k] : 0.f;
+    a.decision[b] = make_float4(__int_as_float(k), row_m[k], row_l[k], 0.f);
+    a.decision_q[b] = make_float4(mq, lq, 0.f, 0.f);
+  }
+}
+
+// The drawn row's weights for sequence b, from the decision record.
+__device__ __forceinline__ void draw_rows(const ChainArgs& a, int b, int& k, DrawRow& dp,
+                                          DrawRow& dr) {
+  const float4 dec = a.decision[b];
+  k = __float_as_int(dec.x);
+  dp.zp = a.target + ((size_t)b * (a.N + 1) + k) * a.V;
+  dp.mp = dec.y;
+  dp.lp = dec.z;
+  dp.c = a.c2;
+  dp.zq = nullptr;
+  dp.mq = dp.lq = 0.f;
+  dr = dp;
+  if (k < a.N) {
+    const float4 dq = a.decision_q[b];
+    dr.zq = a.draft + ((size_t)b * a.N + k) * a.V;
+    dr.mq = dq.x;
+    dr.lq = dq.y;
+  }
+}
+
+template <int VEC>
+__global__ __launch_bounds__(kDrawThreads) void chain_chunks_kernel(ChainArgs a) {
+  __shared__ float wave_tot[kDrawThreads / kWave], wave_off[kDrawThreads / kWave];
+  const int c = blockIdx.x, b = blockIdx.y, nch = a.dchunks;
+  int k;
+  DrawRow dp, dr;
+  draw_rows(a, b, k, dp, dr);
+  float w[kDrawPer], pre[kDrawPer];
+  draw_weights<VEC>(dr, a.V, c, w);
+  chunk_scan(w, pre, wave_tot, wave_off);
+  if (threadIdx.x == kDrawThreads - 1) a.csum[(size_t)b * 2 * nch + c] = pre[kDrawPer - 1];
+}
+
+template <int VEC>
+__global__ __launch_bounds__(kDrawThreads) void chain_select_kernel(ChainArgs a) {
+  __shared__ float wave_tot[kDrawThreads / kWave], wave_off[kDrawThreads / kWave];
+  __shared__ int wave_hit[kDrawThreads / kWave];
+  __shared__ int s_chunk, s_mode, s_y;
+  __shared__ float s_carry, s_target;
+  const int b = blockIdx.x, tid = threadIdx.x, N = a.N, nch = a.dchunks;
+  const int lane = tid & 63, wave = tid >> 6;
+  int k;
+  DrawRow dp, dr;
+  draw_rows(a, b, k, dp, dr);
+  float* cs = a.csum + (size_t)b * 2 * nch;
+  __shared__ float total_s;
+
+  if (tid == 0) {
+    float total = 0.f;
+    for (int i = 0; i < nch; ++i) total += cs[i];
+    total_s = total;
   }
   __syncthreads();
-  const int k = s_k;
-  const int nch = (a.V + kDrawChunk - 1) / kDrawChunk;
-  const float u = a.u_draw[(size_t)b * (N + 1) + k];
-
-  for (int attempt = 0; attempt < 2; ++attempt) {
-    DrawRow dr;
-    dr.zp = a.target + ((size_t)b * (N + 1) + k) * a.V;
-    dr.mp = row_m[k];
-    dr.lp = row_l[k];
-    dr.c = a.c2;
-    dr.zq = nullptr;
-    dr.mq = dr.lq = 0.f;
-    if (s_mode == 1) {
-      dr.zq = a.draft + ((size_t)b * N + k) * a.V;
-      dr.mq = row_m[N + 1 + k];
-      dr.lq = row_l[N + 1 + k];
-    }
-
-    // 3. Chunk sums of the weights.
-    float w[kDrawPer], pre[kDrawPer];
+  int use = 0;
+  if (k < N && total_s == 0.f) {
+    // Empty residual at a rejection (possible only through rounding): the
+    // chunk sums of p_k, computed here with the same scan.
+    use = 1;
     for (int c = 0; c < nch; ++c) {
-      draw_weights<VEC>(dr, a.V, c, w);
+      float w[kDrawPer], pre[kDrawPer];
+      draw_weights<VEC>(dp, a.V, c, w);
       chunk_scan(w, pre, wave_tot, wave_off);
-      if (tid == kDrawThreads - 1) csum[c] = pre[kDrawPer - 1];
-    }
-    __syncthreads();
-    if (tid == 0) {
-      float total = 0.f;
-      for (int c = 0; c < nch; ++c) total += csum[c];
-      s_chunk = -2;
-      if (total == 0.f && s_mode == 1) {
-        s_mode = 0;            // empty residual: fall back to p_k
-      } else {
-        const float target = u * total;
-        float acc = 0.f;
-        s_chunk = -1;
-        for (int c = 0; c < nch; ++c) {
-          if (acc + csum[c] > target) { s_chunk = c; break; }
-          acc += csum[c];
-        }
-        s_carry = acc;
-        s_target = target;
-        if (s_chunk < 0) {      // rounding left no crossing: last chunk with mass
-          for (int c = nch - 1; c >= 0; --c)
-            if (csum[c] > 0.f) { s_chunk = c; break; }
-        }
-      }
-    }
-    __syncthreads();
-    if (s_chunk == -2) continue;   // retry with p_k
-
-    // 4. Locate the crossing inside chunk c: the first weight whose running
-    //    sum exceeds u*total (or, if rounding left no crossing, the last
-    //    positive weight of the last chunk with mass).
-    const int c = s_chunk;
-    if (c < 0) {                    // no mass at all (a row of -inf): no token
-      if (tid == 0) s_y = -1;
+      if (tid == kDrawThreads - 1) cs[nch + c] = pre[kDrawPer - 1];
       __syncthreads();
-      break;
     }
-    const bool last_mass = !(s_carry + csum[c] > s_target);
-    draw_weights<VEC>(dr, a.V, c, w);
+    __threadfence_block();
+    __syncthreads();
+  }
+  if (tid == 0) {
+    const float* row = cs + (size_t)use * nch;
+    float total = 0.f;
+    for (int i = 0; i < nch; ++i) total += row[i];
+    const float target = a.u_draw[(size_t)b * (N + 1) + k] * total;
+    float acc = 0.f;
+    int cstar = -1;
+    for (int i = 0; i < nch; ++i) {
+      if (acc + row[i] > target) { cstar = i; break; }
+      acc += row[i];
+    }
+    if (cstar < 0)                  // rounding left no crossing: last chunk with mass
+      for (int i = nch - 1; i >= 0; --i)
+        if (row[i] > 0.f) { cstar = i; break; }
+    s_mode = use;
+    s_chunk = cstar;
+    s_carry = acc;
+    s_target = target;
+    s_y = -1;
+  }
+  __syncthreads();
+
+  // The crossing inside chunk s_chunk: the first weight whose running sum
+  // exceeds u * total (or the last positive weight if rounding left none).
+  const int cstar = s_chunk;
+  if (cstar >= 0) {
+    const float* row = cs + (size_t)s_mode * nch;
+    const bool last_mass = !(s_carry + row[cstar] > s_target);
+    float w[kDrawPer], pre[kDrawPer];
+    draw_weights<VEC>(s_mode ? dp : dr, a.V, cstar, w);
     chunk_scan(w, pre, wave_tot, wave_off);
     int pick = -1;
     if (!last_mass) {
@@ -297,7 +345,7 @@ __global__ __launch_bounds__(kDrawThreads) void chain_draw_kernel(ChainArgs a) {
       for (int e = 0; e < kDrawPer; ++e)
         if (w[e] > 0.f) pick = e;
     }
-    const int tok = pick < 0 ? -1 : c * kDrawChunk + tid * kDrawPer + pick;
+    const int tok = pick < 0 ? -1 : cstar * kDrawChunk + tid * kDrawPer + pick;
     const uint64_t ballot = __ballot(pick >= 0);
     int src = 0;
     if (ballot) src = last_mass ? 63 - __builtin_clzll(ballot) : __builtin_ctzll(ballot);
@@ -316,10 +364,9 @@ __global__ __launch_bounds__(kDrawThreads) void chain_draw_kernel(ChainArgs a) {
       s_y = y;
     }
     __syncthreads();
-    break;
   }
 
-  // 5. Emit x_0..x_{k-1}, y, then -1.
+  // Emit x_0..x_{k-1}, y, then -1.
   if (tid <= N) {
     int v = -1;
     if (tid < k) v = a.tokens[(size_t)b * N + tid];
@@ -334,8 +381,11 @@ ChainPlan plan_chain(int B, int N, int V) {
   p.rows_per_seq = 2 * N + 1;
   p.chunk = kStatsChunk;
   p.nchunks = (V + kStatsChunk - 1) / kStatsChunk;
+  p.dchunks = (V + kDrawChunk - 1) / kDrawChunk;
   p.stats_bytes = align256((size_t)B * p.rows_per_seq * p.nchunks * sizeof(float2));
-  p.total_bytes = p.stats_bytes;
+  p.csum_bytes = align256((size_t)B * 2 * p.dchunks * sizeof(float));
+  p.decision_bytes = align256((size_t)B * 2 * sizeof(float4));
+  p.total_bytes = p.stats_bytes + p.csum_bytes + p.decision_bytes;
   return p;
 }
 
@@ -347,7 +397,10 @@ hipError_t launch_chain(const ChainPlan& p, const float* target, const float* dr
   a.target = target; a.draft = draft; a.tokens = tokens; a.u_acc = u_acc; a.u_draw = u_draw;
   a.num_acc = num_acc; a.out = out;
   a.stats = (float2*)workspace;
-  a.B = B; a.N = N; a.V = V; a.chunk = p.chunk; a.nchunks = p.nchunks;
+  a.csum = (float*)((char*)workspace + p.stats_bytes);
+  a.decision = (float4*)((char*)workspace + p.stats_bytes + p.csum_bytes);
+  a.decision_q = a.decision + B;
+  a.B = B; a.N = N; a.V = V; a.chunk = p.chunk; a.nchunks = p.nchunks; a.dchunks = p.dchunks;
   a.c2 = kLog2e / temperature;
   const bool vec4 = (V % 4 == 0) && ((uintptr_t)target % 16 == 0) &&
                     (N == 0 || (uintptr_t)draft % 16 == 0);
@@ -356,8 +409,16 @@ hipError_t launch_chain(const ChainPlan& p, const float* target, const float* dr
   else chain_stats_kernel<1><<<g1, kStatsThreads, 0, st>>>(a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  if (vec4) chain_draw_kernel<4><<<B, kDrawThreads, 0, st>>>(a);
-  else chain_draw_kernel<1><<<B, kDrawThreads, 0, st>>>(a);
+  chain_decide_kernel<<<B, 256, 0, st>>>(a);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const dim3 g2(p.dchunks, B);
+  if (vec4) chain_chunks_kernel<4><<<g2, kDrawThreads, 0, st>>>(a);
+  else chain_chunks_kernel<1><<<g2, kDrawThreads, 0, st>>>(a);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if (vec4) chain_select_kernel<4><<<B, kDrawThreads, 0, st>>>(a);
+  else chain_select_kernel<1><<<B, kDrawThreads, 0, st>>>(a);
   return hipGetLastError();
 }
 

@@ -54,8 +54,9 @@ struct AttnPlan {
 struct ChainPlan {
   int rows_per_seq;  // 2N + 1
   int chunk;         // logits per stats block
-  int nchunks;
-  size_t stats_bytes, total_bytes;
+  int nchunks;       // stats chunks per row
+  int dchunks;       // draw chunks per row
+  size_t stats_bytes, csum_bytes, decision_bytes, total_bytes;
 };
 
 struct TreePlan {
