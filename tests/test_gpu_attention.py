@@ -75,10 +75,20 @@ def test_reduced_workloads_elementwise(name):
     ("empty_prefix", dict(T=6, Hq=32, Hkv=8, D=128, ctx=0, dtype="bf16")),
     ("chain_of_64", dict(T=64, Hq=8, Hkv=8, D=128, ctx=65, dtype="bf16")),
     ("gqa_8_mfma_two_row_chunks", dict(T=64, Hq=64, Hkv=8, D=128, ctx=40, dtype="bf16")),
+    # >= 512 (sequence, KV head) units: two key streams per block, merged in-block
+    ("two_key_streams_odd_tiles", dict(B=64, T=9, ctx=70, dtype="bf16")),
+    ("two_key_streams_even_tiles", dict(B=64, T=5, ctx=187, dtype="bf16")),
 ])
 def test_edge_shapes(name, kw):
-    base = I.WORKLOADS["large_batch_chain"].with_(name=name, B=2, kind="chain", seed=11, **kw)
-    run_case(base)
+    args = dict(name=name, B=2, kind="chain", seed=11)
+    args.update(kw)
+    run_case(I.WORKLOADS["large_batch_chain"].with_(**args))
+
+
+def test_two_key_streams_tree():
+    w = I.WORKLOADS["eagle2_tree"].with_(B=64, ctx=150, Hq=16, Hkv=8, T=20,
+                                         tree_widths=(1, 4, 5, 5, 5), seed=15)
+    run_case(w)
 
 
 def test_random_tree_of_64_with_deep_branches():

@@ -325,8 +325,8 @@ __device__ __forceinline__ int pv_key(int g, int e) {
   return (e < 4 ? 4 * g + e : 16 + 4 * g + (e - 4));
 }
 
-template <int D, int RT, int W>
-__global__ __launch_bounds__(64 * W) void attn_mfma_kernel(AttnArgs a) {
+template <int D, int RT, int W, int KS>
+__global__ __launch_bounds__(64 * W * KS) void attn_mfma_kernel(AttnArgs a) {
   constexpr int KT = kMfmaKeys;
   constexpr int KSTR = D + 8;        // bf16 per K row in LDS (+16 B: conflict-free b128 reads)
   constexpr int VSTR = D + 16;       // bf16 per V row in LDS (+32 B: conflict-free tr16 reads)
@@ -335,9 +335,14 @@ __global__ __launch_bounds__(64 * W) void attn_mfma_kernel(AttnArgs a) {
   constexpr int CPR = D / 8;         // 16-byte chunks per key row
   constexpr int NCH = KT * CPR;      // chunks per tile and tensor
   constexpr int NPT = (NCH + 64 * W - 1) / (64 * W);
+  constexpr int TILE_BYTES = KT * (KSTR + VSTR) * 2;
+  static_assert(KS == 1 || KS == 2, "key streams per block");
+  // stream 1's final state goes through LDS: W waves x RT tiles x DT f32x4 x 64 lanes, + (m, l)
+  static_assert(KS == 1 || W * RT * (DT * 64 * 16 + 64 * 8) <= KS * TILE_BYTES, "merge buffer");
 
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[KT * KSTR];
-  __shared__ __attribute__((aligned(16))) uint16_t Vs[KT * VSTR];
+  // Per key stream: a K tile and a V tile.  The buffer is reused at the end
+  // to hand stream 1's state to stream 0.
+  __shared__ __attribute__((aligned(16))) uint8_t tiles[KS * TILE_BYTES];
   __shared__ int par[64];
   __shared__ uint64_t masks[64];
 
@@ -345,8 +350,12 @@ __global__ __launch_bounds__(64 * W) void attn_mfma_kernel(AttnArgs a) {
   const int b = u / a.Hkv, gk = u % a.Hkv;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform (scalar)
+  const int ks = wave / W, wr = wave % W;                       // key stream, row wave
+  const int stid = tid - ks * 64 * W;                           // thread within the stream
   const int l16 = lane & 15, g4 = lane >> 4;
-  const int tile0 = (rc * W + wave) * RT;
+  const int tile0 = (rc * W + wr) * RT;
+  uint16_t* Ks = (uint16_t*)(tiles + ks * TILE_BYTES);
+  uint16_t* Vs = Ks + KT * KSTR;
 
   build_masks(a, b, par, masks);
 
@@ -381,21 +390,25 @@ __global__ __launch_bounds__(64 * W) void attn_mfma_kernel(AttnArgs a) {
     for (int dt = 0; dt < DT; ++dt) acc[rt][dt] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
   }
 
+  // The block's keys [kb, ke) are cut into KS contiguous, tile-aligned parts.
   const int kb = s * a.chunk, ke = min(a.L, kb + a.chunk);
+  const int ntiles = (ke - kb + KT - 1) / KT;
+  const int tps = (ntiles + KS - 1) / KS;                       // tiles per stream
+  const int sb = min(ke, kb + ks * tps * KT), se = min(ke, sb + tps * KT);
   const size_t unit_off = (size_t)u * a.L * D;
   const uint16_t* kg = (const uint16_t*)a.k + unit_off;
   const uint16_t* vg = (const uint16_t*)a.v + unit_off;
   const float c = a.scale_log2;
-  const int clean_end = min(a.ctx, ke);   // tiles ending here need no mask
+  const int clean_end = min(a.ctx, se);   // tiles ending here need no mask
 
-  // Register staging: chunk i*64W + tid of the tile, 16 lanes per key row.
+  // Register staging: chunk i*64W + stid of the tile, 16 lanes per key row.
   // Keys past the end are clamped to the last row (finite data, masked later).
   u32x4_t kreg[NPT], vreg[NPT];
   auto load_tile = [&](int base) {
 #pragma unroll
     for (int i = 0; i < NPT; ++i) {
-      const int ch = i * 64 * W + tid;
-      if (NCH % (64 * W) == 0 || (i * W + wave) * 64 < NCH) {   // uniform per wave
+      const int ch = i * 64 * W + stid;
+      if (NCH % (64 * W) == 0 || (i * W + wr) * 64 < NCH) {   // uniform per wave
         const int key = min(base + ch / CPR, a.L - 1);
         const uint32_t off = (uint32_t)(key * D + 8 * (ch % CPR));
         kreg[i] = *(const u32x4_t*)(kg + off);
@@ -406,8 +419,8 @@ __global__ __launch_bounds__(64 * W) void attn_mfma_kernel(AttnArgs a) {
   auto store_tile = [&]() {
 #pragma unroll
     for (int i = 0; i < NPT; ++i) {
-      const int ch = i * 64 * W + tid;
-      if (NCH % (64 * W) == 0 || (i * W + wave) * 64 < NCH) {
+      const int ch = i * 64 * W + stid;
+      if (NCH % (64 * W) == 0 || (i * W + wr) * 64 < NCH) {
         const int kr = ch / CPR, kc = ch % CPR;
         *(u32x4_t*)(Ks + kr * KSTR + 8 * kc) = kreg[i];
         *(u32x4_t*)(Vs + kr * VSTR + 8 * kc) = vreg[i];
@@ -421,12 +434,16 @@ __global__ __launch_bounds__(64 * W) void attn_mfma_kernel(AttnArgs a) {
   const int vkey0 = pv_key(g4, l16 >> 2), vkey1 = pv_key(g4, 4 + (l16 >> 2));
   const int vcol = 4 * (l16 & 3);
 
-  if (kb < ke) load_tile(kb);
-  for (int base = kb; base < ke; base += KT) {
+  if (sb < se) load_tile(sb);
+  // Every stream runs tps iterations so that all waves meet at each barrier.
+  for (int it = 0; it < tps; ++it) {
+    const int base = sb + it * KT;
+    const bool active = base < se;                              // uniform per stream
     __syncthreads();
-    store_tile();
+    if (active) store_tile();
     __syncthreads();
-    if (base + KT < ke) load_tile(base + KT);
+    if (!active) continue;
+    if (base + KT < se) load_tile(base + KT);
 
     // S^T for the tile's two 16-key halves.
     f32x4_t st[RT][2];
@@ -461,7 +478,7 @@ __global__ __launch_bounds__(64 * W) void attn_mfma_kernel(AttnArgs a) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const int key = base + (e < 4 ? 4 * g4 + e : 16 + 4 * g4 + e - 4);
-          if (!(key < ke && tail_visible(mrow[rt], key, a.ctx))) sc[e] = kNegInf;
+          if (!(key < se && tail_visible(mrow[rt], key, a.ctx))) sc[e] = kNegInf;
         }
       }
       float mt = sc[0];
@@ -511,19 +528,66 @@ __global__ __launch_bounds__(64 * W) void attn_mfma_kernel(AttnArgs a) {
     }
   }
 
-  // Partials: lane holds O^T[16dt + 4g4 + r][row l16] (unnormalised, max m).
+  // Row sums over the four lane groups (every lane of a row gets the total).
+  float lt[RT];
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) {
-    float lt = lpart[rt];
-    lt += __shfl_xor(lt, 16);
-    lt += __shfl_xor(lt, 32);
+    lt[rt] = lpart[rt];
+    lt[rt] += __shfl_xor(lt[rt], 16);
+    lt[rt] += __shfl_xor(lt[rt], 32);
+  }
+
+  if constexpr (KS == 2) {
+    // Stream 1 hands its state to stream 0 through LDS (same row wave, same
+    // lane, same layout), and stream 0 merges the two.
+    __syncthreads();
+    f32x4_t* xo = (f32x4_t*)tiles;
+    float* xm = (float*)(tiles + W * RT * DT * 64 * 16);
+    if (ks == 1) {
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt) {
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) xo[((wr * RT + rt) * DT + dt) * 64 + lane] = acc[rt][dt];
+        xm[((wr * RT + rt) * 64 + lane) * 2] = m[rt];
+        xm[((wr * RT + rt) * 64 + lane) * 2 + 1] = lt[rt];
+      }
+    }
+    __syncthreads();
+    if (ks == 1) return;
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+      const float m2 = xm[((wr * RT + rt) * 64 + lane) * 2];
+      const float l2 = xm[((wr * RT + rt) * 64 + lane) * 2 + 1];
+      const float mx = fmaxf(m[rt], m2);
+      if (mx == kNegInf) continue;
+      const float a1 = fast_exp2(m[rt] - mx), a2 = fast_exp2(m2 - mx);
+      lt[rt] = lt[rt] * a1 + l2 * a2;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+        acc[rt][dt] = acc[rt][dt] * a1 + xo[((wr * RT + rt) * DT + dt) * 64 + lane] * a2;
+      m[rt] = mx;
+    }
+  }
+
+  // Lane holds O^T[16dt + 4g4 + r][row l16]: the final output when the block
+  // saw every key (one split), else an unnormalised partial (o, m, l).
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) {
     const int row = (tile0 + rt) * 16 + l16;
     if (!live[rt] || row >= a.R) continue;
-    const size_t prow = ((size_t)u * a.S + s) * a.R + row;
+    if (a.S == 1) {
+      const int t = row / a.G, h = gk * a.G + row % a.G;
+      float* op = a.out + (((size_t)b * a.T + t) * a.Hq + h) * D + 4 * g4;
+      const float inv = 1.f / lt[rt];
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt)
-      *(f32x4_t*)(a.part_o + prow * D + 16 * dt + 4 * g4) = acc[rt][dt];
-    if (g4 == 0) { a.part_ml[prow * 2] = m[rt]; a.part_ml[prow * 2 + 1] = lt; }
+      for (int dt = 0; dt < DT; ++dt) *(f32x4_t*)(op + 16 * dt) = acc[rt][dt] * inv;
+    } else {
+      const size_t prow = ((size_t)u * a.S + s) * a.R + row;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+        *(f32x4_t*)(a.part_o + prow * D + 16 * dt + 4 * g4) = acc[rt][dt];
+      if (g4 == 0) { a.part_ml[prow * 2] = m[rt]; a.part_ml[prow * 2 + 1] = lt[rt]; }
+    }
   }
 }
 
@@ -555,23 +619,38 @@ __global__ __launch_bounds__(128) void attn_combine_kernel(AttnArgs a) {
 template <int D, int RT>
 static void launch_mfma_w(const AttnPlan& p, const AttnArgs& a, hipStream_t st, dim3 grid) {
   switch (p.waves) {
-    case 1: attn_mfma_kernel<D, RT, 1><<<grid, 64, 0, st>>>(a); break;
-    case 2: attn_mfma_kernel<D, RT, 2><<<grid, 128, 0, st>>>(a); break;
-    case 3: attn_mfma_kernel<D, RT, 3><<<grid, 192, 0, st>>>(a); break;
-    case 4: attn_mfma_kernel<D, RT, 4><<<grid, 256, 0, st>>>(a); break;
-    case 5: attn_mfma_kernel<D, RT, 5><<<grid, 320, 0, st>>>(a); break;
-    case 6: attn_mfma_kernel<D, RT, 6><<<grid, 384, 0, st>>>(a); break;
-    case 7: attn_mfma_kernel<D, RT, 7><<<grid, 448, 0, st>>>(a); break;
-    default: attn_mfma_kernel<D, RT, 8><<<grid, 512, 0, st>>>(a); break;
+    case 1: attn_mfma_kernel<D, RT, 1, 1><<<grid, 64, 0, st>>>(a); break;
+    case 2: attn_mfma_kernel<D, RT, 2, 1><<<grid, 128, 0, st>>>(a); break;
+    case 3: attn_mfma_kernel<D, RT, 3, 1><<<grid, 192, 0, st>>>(a); break;
+    case 4: attn_mfma_kernel<D, RT, 4, 1><<<grid, 256, 0, st>>>(a); break;
+    case 5: attn_mfma_kernel<D, RT, 5, 1><<<grid, 320, 0, st>>>(a); break;
+    case 6: attn_mfma_kernel<D, RT, 6, 1><<<grid, 384, 0, st>>>(a); break;
+    case 7: attn_mfma_kernel<D, RT, 7, 1><<<grid, 448, 0, st>>>(a); break;
+    default: attn_mfma_kernel<D, RT, 8, 1><<<grid, 512, 0, st>>>(a); break;
+  }
+}
+
+template <int D, int KS>
+static void launch_mfma_rt(const AttnPlan& p, const AttnArgs& a, hipStream_t st, dim3 grid) {
+  switch (p.rt) {
+    case 1: launch_mfma_w<D, 1>(p, a, st, grid); break;
+    case 2: launch_mfma_w<D, 2>(p, a, st, grid); break;
+    default: launch_mfma_w<D, 3>(p, a, st, grid); break;
   }
 }
 
 template <int D>
 static void launch_mfma(const AttnPlan& p, const AttnArgs& a, hipStream_t st, dim3 grid) {
-  switch (p.rt) {
-    case 1: launch_mfma_w<D, 1>(p, a, st, grid); break;
-    case 2: launch_mfma_w<D, 2>(p, a, st, grid); break;
-    default: launch_mfma_w<D, 3>(p, a, st, grid); break;
+  // two key streams are planned only with one row tile per wave and <= 4 row waves
+  if (p.kstreams == 2) {
+    switch (p.waves) {
+      case 1: attn_mfma_kernel<D, 1, 1, 2><<<grid, 128, 0, st>>>(a); break;
+      case 2: attn_mfma_kernel<D, 1, 2, 2><<<grid, 256, 0, st>>>(a); break;
+      case 3: attn_mfma_kernel<D, 1, 3, 2><<<grid, 384, 0, st>>>(a); break;
+      default: attn_mfma_kernel<D, 1, 4, 2><<<grid, 512, 0, st>>>(a); break;
+    }
+  } else {
+    launch_mfma_rt<D, 1>(p, a, st, grid);
   }
 }
 
@@ -597,6 +676,9 @@ static void launch_valu(const AttnPlan& p, const AttnArgs& a, hipStream_t st, di
 #ifndef SV_MIN_CHUNK
 #define SV_MIN_CHUNK 256
 #endif
+#ifndef SV_FUSE_UNITS
+#define SV_FUSE_UNITS 512
+#endif
 AttnPlan plan_attention(int B, int T, int Hq, int Hkv, int D, int ctx, int bf16) {
   AttnPlan p{};
   const int G = Hq / Hkv, R = G * T, L = ctx + T, units = B * Hkv;
@@ -610,6 +692,10 @@ AttnPlan plan_attention(int B, int T, int Hq, int Hkv, int D, int ctx, int bf16)
     int waves = (tiles + p.rt - 1) / p.rt;
     p.row_chunks = (waves + 7) / 8;
     p.waves = (waves + p.row_chunks - 1) / p.row_chunks;
+    // With enough (sequence, KV head) units to fill the chip, one block holds
+    // two key streams and merges them itself: one launch, no partials.
+    p.kstreams = 1;
+    if (p.waves <= 4 && units * p.row_chunks >= SV_FUSE_UNITS) p.kstreams = 2;
     tile = kMfmaKeys;
     blocks_target = SV_MFMA_BLOCKS;
   } else {
@@ -622,6 +708,7 @@ AttnPlan plan_attention(int B, int T, int Hq, int Hkv, int D, int ctx, int bf16)
   }
   const int min_chunk = SV_MIN_CHUNK;
   int S = (blocks_target + units * p.row_chunks - 1) / (units * p.row_chunks);
+  if (p.mfma && p.kstreams == 2) S = 1;
   const int s_max = (L + min_chunk - 1) / min_chunk;
   if (S > s_max) S = s_max;
   if (S < 1) S = 1;
@@ -659,7 +746,7 @@ hipError_t launch_attention(const AttnPlan& p, const void* q, const void* k, con
     else launch_valu<float, 128>(p, a, st, grid);
   }
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  if (e != hipSuccess || (p.mfma && p.splits == 1)) return e;
   attn_combine_kernel<<<dim3(p.rows, B * Hkv), D, 0, st>>>(a);
   return hipGetLastError();
 }
