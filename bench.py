@@ -15,6 +15,7 @@ bounded sample of the same workload.
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import math
 import os
@@ -28,6 +29,9 @@ if ROOT not in sys.path:
 METRIC = ("verify-step µs + achieved HBM GB/s (attn, sampler) at N=4/8; α overhead")
 HBM_PEAK_GBPS = 8000.0
 WORKLOAD = "large_batch_chain"
+ATTN_SOURCE = os.path.join(ROOT, "verify_pass_rejection_amd", "csrc", "attention.hip")
+TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "attention_large_batch_chain_hbm_traffic.txt")
+COPY_CALIBRATION_BYTES = 1 << 30     # one plain copy of 1 GiB (read 1 GiB, write 1 GiB)
 
 
 def attention_bytes(w) -> int:
@@ -149,6 +153,49 @@ def cpu_baseline(w, step, budget_s: float = 30.0):
                       f"included; {dt:.1f} s"}
 
 
+def source_sha256(path: str) -> str:
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def measured_traffic():
+    """HBM bytes per attention launch from the committed PMC summary, or None
+    if there is none or the kernel source changed since it was taken.
+
+    traffic = FETCH_SIZE * (copy bytes / copy FETCH_SIZE)
+            + WRITE_SIZE * (copy bytes / copy WRITE_SIZE), per dispatch.
+    """
+    if not os.path.exists(TRAFFIC_PROFILE):
+        return None
+    kv = {}
+    for line in open(TRAFFIC_PROFILE):
+        if ":" in line and not line.startswith("#"):
+            key, val = line.split(":", 1)
+            kv[key.strip()] = val.strip()
+    try:
+        if kv.get("attention_source_sha256") != source_sha256(ATTN_SOURCE):
+            return None
+        copy = float(kv["copy_bytes"])
+        fetch = float(kv["attention_fetch_kib"]) * copy / float(kv["copy_fetch_kib"])
+        write = float(kv["attention_write_kib"]) * copy / float(kv["copy_write_kib"])
+        return int(round(fetch + write))
+    except (KeyError, ValueError, ZeroDivisionError):
+        return None
+
+
+def copy_calibration(dev):
+    """A plain device copy of a known size, for scaling the HBM byte counters."""
+    import torch
+    n = COPY_CALIBRATION_BYTES // 4
+    src = torch.ones(n, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
+    torch.cuda.empty_cache()
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -156,6 +203,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-alpha", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain 1 GiB device copy (for scaling byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -167,6 +216,8 @@ def main():
     from verify_pass_rejection_amd import inputs as I
 
     dev = torch.device("cuda:0")
+    if args.copy_calibration:
+        copy_calibration(dev)
     w = I.WORKLOADS[WORKLOAD]
     step = Step(w, dev)
     t = time_steps(step, args.steps, args.warmup)
@@ -221,8 +272,9 @@ def main():
         **alphas,
         "roofline": {"bound": "hbm", "achieved": round(attn_gbps, 1), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(attn_gbps / HBM_PEAK_GBPS, 4),
-                     "traffic": None,
-                     "kernel": "spec_verify_attention (split-K MFMA kernel + split combine)",
+                     "traffic": measured_traffic(),
+                     "kernel": "attn_mfma_kernel (spec_verify_attention: one launch, two key "
+                               "streams per block)",
                      "algorithmic_bytes_per_launch": ab},
         "cpu_baseline": cpu,
     }
