@@ -55,8 +55,11 @@ struct ChainArgs {
 #endif
 constexpr int kStatsThreads = SV_STATS_THREADS;
 constexpr int kStatsChunk = SV_STATS_CHUNK;   // logits per stats block
+#ifndef SV_DRAW_PER
+#define SV_DRAW_PER 8
+#endif
 constexpr int kDrawThreads = 1024;
-constexpr int kDrawPer = 4;           // weights per thread per draw chunk
+constexpr int kDrawPer = SV_DRAW_PER; // weights per thread per draw chunk
 constexpr int kDrawChunk = kDrawThreads * kDrawPer;
 
 __device__ __forceinline__ const float* chain_row(const ChainArgs& a, int b, int rho) {
@@ -138,13 +141,17 @@ __device__ __forceinline__ void draw_weights(const DrawRow& r, int V, int chunk,
   const int j0 = chunk * kDrawChunk + threadIdx.x * kDrawPer;
   float xp[kDrawPer], xq[kDrawPer];
   if constexpr (VEC == 4) {
-    float4 p4 = {kNegInf, kNegInf, kNegInf, kNegInf}, q4 = p4;
-    if (j0 < V) {
-      p4 = *(const float4*)(r.zp + j0);
-      if (r.zq) q4 = *(const float4*)(r.zq + j0);
+    static_assert(kDrawPer % 4 == 0, "whole float4 per thread");
+#pragma unroll
+    for (int i = 0; i < kDrawPer; i += 4) {
+      float4 p4 = {kNegInf, kNegInf, kNegInf, kNegInf}, q4 = p4;
+      if (j0 + i < V) {                 // V % 4 == 0 on this path: all four in range
+        p4 = *(const float4*)(r.zp + j0 + i);
+        if (r.zq) q4 = *(const float4*)(r.zq + j0 + i);
+      }
+      xp[i] = p4.x; xp[i + 1] = p4.y; xp[i + 2] = p4.z; xp[i + 3] = p4.w;
+      xq[i] = q4.x; xq[i + 1] = q4.y; xq[i + 2] = q4.z; xq[i + 3] = q4.w;
     }
-    xp[0] = p4.x; xp[1] = p4.y; xp[2] = p4.z; xp[3] = p4.w;
-    xq[0] = q4.x; xq[1] = q4.y; xq[2] = q4.z; xq[3] = q4.w;
   } else {
 #pragma unroll
     for (int e = 0; e < kDrawPer; ++e) {
@@ -196,6 +203,18 @@ __global__ __launch_bounds__(256) void chain_decide_kernel(ChainArgs a) {
   const int N = a.N, rows = 2 * N + 1;
   const int lane = tid & 63, wave = tid >> 6;
 
+  // The drafted tokens' logits are gathered first so that their latency
+  // overlaps the merge of the chunk statistics.
+  int x = -1;
+  float zp = 0.f, zq = 0.f;
+  if (tid < N) {
+    x = a.tokens[(size_t)b * N + tid];
+    if (x >= 0 && x < a.V) {
+      zp = a.target[((size_t)b * (N + 1) + tid) * a.V + x];
+      zq = a.draft[((size_t)b * N + tid) * a.V + x];
+    }
+  }
+
   // Row normalisers: one wave per row merges the row's chunk statistics in a
   // fixed tree order (lane-strided partial merges, then a butterfly).
   for (int r = wave; r < rows; r += 4) {
@@ -213,11 +232,8 @@ __global__ __launch_bounds__(256) void chain_decide_kernel(ChainArgs a) {
 
   // Ratio tests: keep x_i iff u < p_i(x_i)/q_i(x_i).
   if (tid < N) {
-    const int x = a.tokens[(size_t)b * N + tid];
     bool ok = false;
     if (x >= 0 && x < a.V) {
-      const float zp = a.target[((size_t)b * (N + 1) + tid) * a.V + x];
-      const float zq = a.draft[((size_t)b * N + tid) * a.V + x];
       const float lp = (zp - row_m[tid]) * a.c2 - row_l[tid];
       const float lq = (zq - row_m[N + 1 + tid]) * a.c2 - row_l[N + 1 + tid];
       const float r = exp2f(lp - lq);   // q = 0: +inf when p > 0; NaN (reject) when both 0
@@ -282,10 +298,15 @@ __global__ __launch_bounds__(kDrawThreads) void chain_select_kernel(ChainArgs a)
   draw_rows(a, b, k, dp, dr);
   float* cs = a.csum + (size_t)b * 2 * nch;
   __shared__ float total_s;
+  __shared__ float cs_l[kDrawThreads];
+  const bool in_lds = nch <= kDrawThreads;
+  if (in_lds && tid < nch) cs_l[tid] = cs[tid];           // one parallel load
+  const float u = a.u_draw[(size_t)b * (N + 1) + k];
+  __syncthreads();
 
   if (tid == 0) {
     float total = 0.f;
-    for (int i = 0; i < nch; ++i) total += cs[i];
+    for (int i = 0; i < nch; ++i) total += in_lds ? cs_l[i] : cs[i];
     total_s = total;
   }
   __syncthreads();
@@ -305,10 +326,10 @@ __global__ __launch_bounds__(kDrawThreads) void chain_select_kernel(ChainArgs a)
     __syncthreads();
   }
   if (tid == 0) {
-    const float* row = cs + (size_t)use * nch;
+    const float* row = (use == 0 && in_lds) ? cs_l : cs + (size_t)use * nch;
     float total = 0.f;
     for (int i = 0; i < nch; ++i) total += row[i];
-    const float target = a.u_draw[(size_t)b * (N + 1) + k] * total;
+    const float target = u * total;
     float acc = 0.f;
     int cstar = -1;
     for (int i = 0; i < nch; ++i) {
@@ -330,7 +351,7 @@ __global__ __launch_bounds__(kDrawThreads) void chain_select_kernel(ChainArgs a)
   // exceeds u * total (or the last positive weight if rounding left none).
   const int cstar = s_chunk;
   if (cstar >= 0) {
-    const float* row = cs + (size_t)s_mode * nch;
+    const float* row = (s_mode == 0 && in_lds) ? cs_l : cs + (size_t)s_mode * nch;
     const bool last_mass = !(s_carry + row[cstar] > s_target);
     float w[kDrawPer], pre[kDrawPer];
     draw_weights<VEC>(s_mode ? dp : dr, a.V, cstar, w);
