@@ -47,7 +47,10 @@ def attention_flops(w) -> int:
 
 
 def sampler_bytes(w) -> int:
-    """Algorithmic bytes of chain acceptance: every target and draft logit once."""
+    """Algorithmic bytes of acceptance: every logit once — target and draft rows
+    for a chain, one target row per node for a tree."""
+    if w.kind == "tree":
+        return w.T * w.V * 4 * w.B
     return (2 * w.N + 1) * w.V * 4 * w.B
 
 
@@ -65,26 +68,36 @@ class Step:
         from verify_pass_rejection_amd import native as nat
         self.w, self.nat = w, nat
         self.q, self.k, self.v = I.make_attention_inputs(w, dev)
-        self.d = I.make_chain_inputs(w, dev)
+        self.tree = w.kind == "tree"
+        self.d = I.make_tree_inputs(w, dev) if self.tree else I.make_chain_inputs(w, dev)
+        self.parents = self.d["parents"] if self.tree else None
         self.out = torch.empty((w.B, w.T, w.Hq, w.D), dtype=torch.float32, device=dev)
         self.num = torch.empty(w.B, dtype=torch.int32, device=dev)
         self.tok = torch.empty((w.B, w.T), dtype=torch.int32, device=dev)
+        self.path = torch.empty((w.B, w.T), dtype=torch.int32, device=dev)
         dt = nat.SPEC_BF16 if w.dtype == "bf16" else nat.SPEC_F32
         self.ws_a = torch.empty(nat.spec_verify_attention_workspace(
             w.B, w.T, w.Hq, w.Hkv, w.D, w.ctx, dt), dtype=torch.uint8, device=dev)
-        self.ws_c = torch.empty(max(nat.spec_accept_chain_workspace(w.B, w.N, w.V), 1),
-                                dtype=torch.uint8, device=dev)
+        ws = (nat.spec_accept_tree_workspace(w.B, w.T, w.V) if self.tree
+              else nat.spec_accept_chain_workspace(w.B, w.N, w.V))
+        self.ws_c = torch.empty(max(ws, 1), dtype=torch.uint8, device=dev)
         torch.cuda.synchronize()
 
     def attention(self):
-        self.nat.spec_verify_attention(self.q, self.k, self.v, self.w.ctx, out=self.out,
-                                       workspace=self.ws_a)
+        self.nat.spec_verify_attention(self.q, self.k, self.v, self.w.ctx, parents=self.parents,
+                                       out=self.out, workspace=self.ws_a)
 
     def accept(self):
         d = self.d
-        self.nat.spec_accept_chain(d["target_logits"], d["draft_logits"], d["draft_tokens"],
-                                   d["u_accept"], d["u_draw"], num_accepted=self.num,
-                                   out_tokens=self.tok, workspace=self.ws_c)
+        if self.tree:
+            self.nat.spec_accept_tree(d["target_logits"], d["tokens"], d["parents"],
+                                      accept_len=self.num, path=self.path, out_tokens=self.tok,
+                                      workspace=self.ws_c)
+        else:
+            self.nat.spec_accept_chain(d["target_logits"], d["draft_logits"],
+                                       d["draft_tokens"], d["u_accept"], d["u_draw"],
+                                       num_accepted=self.num, out_tokens=self.tok,
+                                       workspace=self.ws_c)
 
     def __call__(self):
         self.attention()
@@ -205,6 +218,9 @@ def main():
     ap.add_argument("--no-alpha", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (for scaling byte counters)")
+    ap.add_argument("--workload", default=WORKLOAD,
+                    help="reference workload to time (the bench line uses large_batch_chain; "
+                         "the others are for per-kernel measurement)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -218,9 +234,10 @@ def main():
     dev = torch.device("cuda:0")
     if args.copy_calibration:
         copy_calibration(dev)
-    w = I.WORKLOADS[WORKLOAD]
+    w = I.WORKLOADS[args.workload]
     step = Step(w, dev)
     t = time_steps(step, args.steps, args.warmup)
+    mean_accepted = float(step.num.float().mean())
 
     ab, sb = attention_bytes(w), sampler_bytes(w)
     attn_gbps = ab / (t["attn_ms"] * 1e-3) / 1e9
@@ -228,7 +245,7 @@ def main():
     step_gbps = (ab + sb) / (t["ms_per_step"] * 1e-3) / 1e9
 
     alphas = {}
-    if not args.no_alpha:
+    if not args.no_alpha and w.kind == "chain":
         times = {w.N: t["ms_per_step"]}
         del step
         torch.cuda.empty_cache()
@@ -243,7 +260,7 @@ def main():
         step = Step(w, dev)
 
     cpu = None
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and w.kind == "chain":
         cpu = cpu_baseline(w, step)
 
     line = {
@@ -264,6 +281,8 @@ def main():
         "verify_step_us": round(t["ms_per_step"] * 1e3, 2),
         "attn_us": round(t["attn_ms"] * 1e3, 2),
         "sampler_us": round(t["accept_ms"] * 1e3, 2),
+        "acceptance": "greedy tree" if w.kind == "tree" else "chain rejection sampling",
+        "mean_accepted": round(mean_accepted, 3),
         "attn_GBps": round(attn_gbps, 1),
         "sampler_GBps": round(samp_gbps, 1),
         "attn_frac_hbm_peak": round(attn_gbps / HBM_PEAK_GBPS, 4),
@@ -272,7 +291,7 @@ def main():
         **alphas,
         "roofline": {"bound": "hbm", "achieved": round(attn_gbps, 1), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(attn_gbps / HBM_PEAK_GBPS, 4),
-                     "traffic": measured_traffic(),
+                     "traffic": measured_traffic() if w.name == WORKLOAD else None,
                      "kernel": "attn_mfma_kernel (spec_verify_attention: one launch, two key "
                                "streams per block)",
                      "algorithmic_bytes_per_launch": ab},
