@@ -292,8 +292,8 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(attn_gbps, 1), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(attn_gbps / HBM_PEAK_GBPS, 4),
                      "traffic": measured_traffic() if w.name == WORKLOAD else None,
-                     "kernel": "attn_mfma_kernel (spec_verify_attention: one launch, two key "
-                               "streams per block)",
+                     "kernel": "attn_mfma_kernel (spec_verify_attention: one launch, one "
+                               "split per (sequence, KV head))",
                      "algorithmic_bytes_per_launch": ab},
         "cpu_baseline": cpu,
     }

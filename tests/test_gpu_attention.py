@@ -66,18 +66,24 @@ def test_reduced_workloads_elementwise(name):
 
 
 @pytest.mark.parametrize("name,kw", [
-    ("decode_step_T1_bf16_valu", dict(T=1, Hq=32, Hkv=8, D=128, ctx=1500, dtype="bf16")),
+    ("decode_step_T1_bf16_one_row_tile", dict(T=1, Hq=32, Hkv=8, D=128, ctx=1500, dtype="bf16")),
     ("decode_step_T1_f32", dict(T=1, Hq=8, Hkv=8, D=64, ctx=333, dtype="f32")),
     ("f32_rows_over_8_row_chunks", dict(T=5, Hq=16, Hkv=4, D=128, ctx=200, dtype="f32")),
-    ("bf16_12_rows_valu_two_chunks", dict(T=3, Hq=32, Hkv=8, D=128, ctx=700, dtype="bf16")),
+    ("bf16_12_rows_part_empty_tile", dict(T=3, Hq=32, Hkv=8, D=128, ctx=700, dtype="bf16")),
     ("bf16_d64_mfma", dict(T=8, Hq=16, Hkv=4, D=64, ctx=450, dtype="bf16")),
-    ("bf16_d64_valu", dict(T=2, Hq=8, Hkv=4, D=64, ctx=90, dtype="bf16")),
+    ("bf16_d64_4_rows", dict(T=2, Hq=8, Hkv=4, D=64, ctx=90, dtype="bf16")),
     ("empty_prefix", dict(T=6, Hq=32, Hkv=8, D=128, ctx=0, dtype="bf16")),
     ("chain_of_64", dict(T=64, Hq=8, Hkv=8, D=128, ctx=65, dtype="bf16")),
     ("gqa_8_mfma_two_row_chunks", dict(T=64, Hq=64, Hkv=8, D=128, ctx=40, dtype="bf16")),
-    # >= 512 (sequence, KV head) units: two key streams per block, merged in-block
-    ("two_key_streams_odd_tiles", dict(B=64, T=9, ctx=70, dtype="bf16")),
-    ("two_key_streams_even_tiles", dict(B=64, T=5, ctx=187, dtype="bf16")),
+    # >= 512 (sequence, KV head) units: one split per unit, output written directly
+    ("one_split_odd_tiles", dict(B=64, T=9, ctx=70, dtype="bf16")),
+    ("one_split_even_tiles", dict(B=64, T=5, ctx=187, dtype="bf16")),
+    # a single key tile per block, and a key range that fills the LDS ring exactly
+    ("one_key_tile", dict(T=3, Hq=32, Hkv=8, D=128, ctx=5, dtype="bf16")),
+    ("ring_of_tiles_exact", dict(B=64, T=8, ctx=248, dtype="bf16")),
+    # two and three 16-row tiles per wave at D = 64
+    ("d64_two_row_tiles", dict(T=32, Hq=64, Hkv=8, D=64, ctx=333, dtype="bf16")),
+    ("d64_three_row_tiles", dict(T=40, Hq=64, Hkv=8, D=64, ctx=260, dtype="bf16")),
 ])
 def test_edge_shapes(name, kw):
     args = dict(name=name, B=2, kind="chain", seed=11)
@@ -85,7 +91,7 @@ def test_edge_shapes(name, kw):
     run_case(I.WORKLOADS["large_batch_chain"].with_(**args))
 
 
-def test_two_key_streams_tree():
+def test_one_split_tree():
     w = I.WORKLOADS["eagle2_tree"].with_(B=64, ctx=150, Hq=16, Hkv=8, T=20,
                                          tree_widths=(1, 4, 5, 5, 5), seed=15)
     run_case(w)

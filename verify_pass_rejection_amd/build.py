@@ -28,10 +28,17 @@ CFLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
           "-I", os.path.join(ROOT, "include"), "-Wall", "-Wno-unused-function"]
 
 
+# Per-file additions.  The attention kernels never produce or consume NaN
+# (masked scores are -inf and every guard compares before subtracting), so
+# max/min need no NaN-quieting of lane-swapped operands.
+FILE_FLAGS = {"attention.hip": ["-fno-honor-nans"]}
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, src + ".o")
     lang = [] if src.endswith(".hip") else ["-x", "hip"]
-    cmd = [HIPCC, *CFLAGS, *lang, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC, *CFLAGS, *FILE_FLAGS.get(src, []), *lang, "-c", os.path.join(CSRC, src),
+           "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stdout}\n{r.stderr}")

@@ -16,17 +16,21 @@
 //  * the tree mask is the ancestor-or-self bitmask of each query position,
 //    one u64 per row held in registers: key ctx + t is visible to row i iff
 //    bit t of mask(i) is set; prefix keys are visible to every row;
-//  * R < 16 (or fp32 inputs): VALU kernel, 16-byte loads, one key row spread
-//    over D*sizeof/16 lanes, scores reduced across those lanes;
-//  * bf16 with R >= 16: MFMA kernel (v_mfma_f32_16x16x32_bf16).  Scores are
-//    computed transposed, S^T = K Q^T, and the output as O^T += V^T P^T, so the
-//    probabilities produced by the first product are already in the operand
-//    layout of the second: no cross-lane shuffle of P.  K and V are staged in
-//    LDS row-major; the V operand, which needs four consecutive keys per lane,
-//    is read with the gfx950 transposing LDS load (ds_read_tr16_b64).
+//  * fp32 inputs: VALU kernel, 16-byte loads, one key row spread over D/4
+//    lanes, scores reduced across those lanes;
+//  * bf16: MFMA kernel (v_mfma_f32_16x16x32_bf16), whatever R (a part-empty
+//    row tile costs matrix work only; the pass is bound by the K/V stream).
+//    Scores are computed transposed, S^T = K Q^T, and the output as
+//    O^T += V^T P^T, so the probabilities produced by the first product are
+//    already in the operand layout of the second: no cross-lane shuffle of P.
+//    A loader wave streams K and V into an LDS ring with direct-to-LDS loads;
+//    the V operand, which needs four consecutive keys per lane, is read with
+//    the gfx950 transposing LDS load (ds_read_tr16_b64).
 //
 // Scores are kept in the log2 domain (scale * log2(e) folded in) and
 // exponentiated with the hardware exp2.
+
+#include <type_traits>
 
 #include "common.h"
 
@@ -80,18 +84,16 @@ __device__ __forceinline__ bool tail_visible(uint64_t mask, int key, int ctx) {
   return key < ctx || ((mask >> (key - ctx)) & 1ull);
 }
 
-#ifndef SV_SETTLE_MFMA
-#define SV_SETTLE_MFMA 1
-#endif
-#ifndef SV_MFMA_WAVES_PER_EU
-#define SV_MFMA_WAVES_PER_EU 4
-#endif
 #ifndef SV_SETTLE_VALU
 #define SV_SETTLE_VALU 1
 #endif
 #ifndef SV_VALU_WAVES_PER_EU
 #define SV_VALU_WAVES_PER_EU 1
 #endif
+
+// Lambdas of the kernels are always inlined: an out-of-line call inside the
+// key loop would make the compiler drain every outstanding load at its return.
+#define SV_INLINE __attribute__((always_inline))
 
 // Marks registers as used here, so the compiler waits for their loads once,
 // before a loop, instead of re-checking (and draining newer loads) inside it.
@@ -113,15 +115,13 @@ __device__ __forceinline__ void merge_state(float& m, float& l, float m2, float 
 }
 
 // ---------------------------------------------------------------------------
-// VALU kernel: 4 independent waves per block; grid (S, B*Hkv, ceil(R / RMAX)).
-// A key row is spread over LPK lanes (one 16-byte load each); bf16 scores use
-// v_dot2_f32_bf16 and are summed across the LPK lanes with a DPP butterfly,
+// VALU kernel (fp32 inputs): 4 independent waves per block; grid (S, B*Hkv,
+// ceil(R / RMAX)).  A key row is spread over LPK lanes (one 16-byte load
+// each); partial scores are summed across the LPK lanes with a DPP butterfly,
 // which leaves the bit-identical total in every lane of the group.  Each lane
 // group keeps its own online-softmax state over its keys; the groups and the
 // waves are merged at the end.
 // ---------------------------------------------------------------------------
-typedef __bf16 bf16x2v_t __attribute__((ext_vector_type(2)));
-
 template <int CTRL>
 __device__ __forceinline__ float dpp_f(float v) {
   return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xf, 0xf, false));
@@ -139,12 +139,11 @@ __device__ __forceinline__ float group_sum(float v) {
   return v;
 }
 
-template <typename TIn, int D, int RMAX>
+template <int D, int RMAX>
 __global__ __launch_bounds__(256)
 __attribute__((amdgpu_waves_per_eu(RMAX <= 4 ? SV_VALU_WAVES_PER_EU : 1)))
 void attn_valu_kernel(AttnArgs a) {
-  constexpr bool BF = sizeof(TIn) == 2;
-  constexpr int EPL = 16 / (int)sizeof(TIn);  // elements per lane per 16-byte load
+  constexpr int EPL = 4;                      // fp32 elements per lane per 16-byte load
   constexpr int LPK = D / EPL;                // lanes sharing one key row
   constexpr int KPS = kWave / LPK;            // keys per wave step
   constexpr int U = 4;                        // key steps per iteration
@@ -166,7 +165,7 @@ void attn_valu_kernel(AttnArgs a) {
 
   build_masks(a, b, par, masks);
 
-  // Query rows: raw bf16 pairs (dot2 operands) or fp32 values.
+  // Query rows (fp32 bits).
   u32x4_t qw[RMAX];
   uint64_t mrow[RMAX];
 #pragma unroll
@@ -175,7 +174,7 @@ void attn_valu_kernel(AttnArgs a) {
     mrow[r] = 0;
     if (r < nr) {
       const int row = r0 + r, t = row / a.G, h = g * a.G + row % a.G;
-      qw[r] = *(const u32x4_t*)((const TIn*)a.q + (((size_t)b * a.T + t) * a.Hq + h) * D +
+      qw[r] = *(const u32x4_t*)((const float*)a.q + (((size_t)b * a.T + t) * a.Hq + h) * D +
                                 dp * EPL);
       mrow[r] = masks[t];
     }
@@ -203,8 +202,8 @@ void attn_valu_kernel(AttnArgs a) {
   }
 
   const size_t unit_off = (size_t)u * a.L * D;
-  const TIn* kp = (const TIn*)a.k + unit_off + dp * EPL;
-  const TIn* vp = (const TIn*)a.v + unit_off + dp * EPL;
+  const float* kp = (const float*)a.k + unit_off + dp * EPL;
+  const float* vp = (const float*)a.v + unit_off + dp * EPL;
   const int last = a.L - 1;
 
   u32x4_t kw[U], vw[U];
@@ -225,18 +224,9 @@ void attn_valu_kernel(AttnArgs a) {
 
     float vf[U][EPL];
 #pragma unroll
-    for (int j = 0; j < U; ++j) {
-      if constexpr (BF) {
+    for (int j = 0; j < U; ++j)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          vf[j][2 * e] = bf16_lo(vcur[j][e]);
-          vf[j][2 * e + 1] = bf16_hi(vcur[j][e]);
-        }
-      } else {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) vf[j][e] = __uint_as_float(vcur[j][e]);
-      }
-    }
+      for (int e = 0; e < 4; ++e) vf[j][e] = __uint_as_float(vcur[j][e]);
     const bool clean = key0 + KPI <= clean_end;
 #pragma unroll
     for (int r = 0; r < RMAX; ++r) {
@@ -245,21 +235,9 @@ void attn_valu_kernel(AttnArgs a) {
 #pragma unroll
       for (int j = 0; j < U; ++j) {
         float acc = 0.f;
-        if constexpr (BF) {
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            // copy the vector elements out first: a bit_cast of an ext-vector
-            // element expression reads element 0 whatever the index
-            const uint32_t qe = qw[r][e], ke2 = kcur[j][e];
-            acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2v_t, qe),
-                                                  __builtin_bit_cast(bf16x2v_t, ke2), acc,
-                                                  false);
-          }
-        } else {
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            acc = fmaf(__uint_as_float(qw[r][e]), __uint_as_float(kcur[j][e]), acc);
-        }
+        for (int e = 0; e < 4; ++e)
+          acc = fmaf(__uint_as_float(qw[r][e]), __uint_as_float(kcur[j][e]), acc);
         sc[j] = group_sum<LPK>(acc);
         if (!clean) {
           const int key = key0 + j * KPS + ks;
@@ -349,29 +327,105 @@ __device__ __forceinline__ int pv_key(int g, int e) {
   return (e < 4 ? 4 * g + e : 16 + 4 * g + (e - 4));
 }
 
-// One row tile per wave: ask for the occupancy that keeps two blocks per CU
-// resident (measured: 1.39 ms vs 1.50 ms on the 64 x 32768 batch).  Larger
-// row tiles need their registers (forcing occupancy there spills).
-template <int D, int RT, int W, int KS>
-__global__ __launch_bounds__(64 * W * KS)
-__attribute__((amdgpu_waves_per_eu(RT == 1 ? SV_MFMA_WAVES_PER_EU : 1)))
+// Reductions over the four 16-lane groups of a wave (lanes l, l^16, l^32,
+// l^48), every lane receiving the result.  The gfx950 lane-swap instructions
+// exchange rows 1,3 with rows 0,2 of a second register (permlane16) and the
+// upper with the lower half (permlane32); combining each pair gives the
+// xor-16 / xor-32 partner without going through LDS.
+__device__ __forceinline__ float group4_max(float x) {
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float group4_sum(float x) {
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Loading.  The block is W compute waves plus one loader wave.  The loader
+// streams the block's key range through a ring of P LDS slots of one 32-key
+// K/V tile each with direct-to-LDS loads (global_load_lds, 16 bytes per lane
+// written straight into LDS), keeping AHEAD = P - 1 tiles in flight without
+// holding them in registers.  It waits for its own loads (s_waitcnt vmcnt)
+// and joins the block barrier: after barrier j, tile j is complete in slot
+// j % P and the slot of tile j-1 is free for tile j + AHEAD.  The compute
+// waves issue no global loads inside the key loop.  The loads are written as
+// inline assembly so that the compiler does not order LDS reads after them.
+//
+// Slot layout.  A direct-to-LDS load writes 1 KB contiguous (lane L at +16L),
+// here a group of KG = 512/D key rows.  Inside a group the 16-byte chunks are
+// placed by chunk_pos() so that the V fragment reads (ds_read_tr16_b64) are
+// free of bank conflicts and the K fragment reads (ds_read_b128) spread over
+// all banks; groups are padded to GSK / GSV bytes.
+//   D = 128 (4 rows x 16 chunks): chunk c of row j at 4c + j;
+//   D = 64  (8 rows x 8 chunks):  16(c/2) + 8(j/4) + ((4(c%2) + j%4) ^ 4(j/4)).
+template <int D>
+struct MfmaLayout {
+  static constexpr int KT = kMfmaKeys;
+  static constexpr int KG = 512 / D;              // key rows per 1 KB group
+  static constexpr int NG = KT / KG;              // groups per tile and tensor
+  static constexpr int GSK = D == 128 ? 1088 : 1152;
+  static constexpr int GSV = 1152;
+  static constexpr int KHALF = NG * GSK;
+  static constexpr int SLOT = KHALF + NG * GSV;
+  static constexpr int NIT = 2 * NG;              // 1 KB loads per tile (K and V)
+  __host__ __device__ static constexpr int chunk_pos(int j, int c) {
+    return D == 128 ? 4 * c + j
+                    : 16 * (c >> 1) + 8 * (j >> 2) + ((4 * (c & 1) + (j & 3)) ^ (4 * (j >> 2)));
+  }
+};
+
+// Ring depth: four slots (72 KB at D = 128) keep two blocks per CU resident
+// for one-row-tile kernels; five for the larger ones (one block per CU).  The
+// loader's outstanding loads, (AHEAD - 1) * NIT, must fit the 6-bit vmcnt.
+template <int D, int RT>
+struct MfmaRing {
+  static constexpr int P = RT == 1 ? 4 : 5;
+  static constexpr int AHEAD = P - 1;
+  static_assert((AHEAD - 1) * MfmaLayout<D>::NIT < 64, "vmcnt range");
+};
+
+// One direct load of 16 bytes per lane into LDS at byte offset lds (wave-
+// uniform; lane L writes lds + 16L).  M0 carries the LDS address; the nop
+// covers the M0-write to LDS-DMA hazard.
+__device__ __forceinline__ void lds_dma16(const void* g, uint32_t lds) {
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "{m0}"(lds) : "memory");
+}
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+// Wait until at most `rem` (<= MAXR, wave-uniform) tiles of C loads each are
+// still outstanding (this wave's loads only).
+template <int C, int MAXR>
+__device__ __forceinline__ void wait_tiles(int rem) {
+  if constexpr (MAXR == 0) {
+    wait_vm<0>();
+  } else {
+    if (rem >= MAXR) wait_vm<MAXR * C>();
+    else wait_tiles<C, MAXR - 1>(rem);
+  }
+}
+// Block barrier for the ring: LDS reads done, then s_barrier.  The memory
+// clobber keeps every LDS access on its side of the barrier.
+__device__ __forceinline__ void ring_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+template <int D, int RT, int W>
+__global__ __launch_bounds__(64 * (W + 1))
 void attn_mfma_kernel(AttnArgs a) {
+  using LY = MfmaLayout<D>;
+  using RG = MfmaRing<D, RT>;
   constexpr int KT = kMfmaKeys;
-  constexpr int KSTR = D + 8;        // bf16 per K row in LDS (+16 B: conflict-free b128 reads)
-  constexpr int VSTR = D + 16;       // bf16 per V row in LDS (+32 B: conflict-free tr16 reads)
+  constexpr int P = RG::P;
   constexpr int DT = D / 16;
   constexpr int KK = D / 32;
-  constexpr int CPR = D / 8;         // 16-byte chunks per key row
-  constexpr int NCH = KT * CPR;      // chunks per tile and tensor
-  constexpr int NPT = (NCH + 64 * W - 1) / (64 * W);
-  constexpr int TILE_BYTES = KT * (KSTR + VSTR) * 2;
-  static_assert(KS == 1 || KS == 2, "key streams per block");
-  // stream 1's final state goes through LDS: W waves x RT tiles x DT f32x4 x 64 lanes, + (m, l)
-  static_assert(KS == 1 || W * RT * (DT * 64 * 16 + 64 * 8) <= KS * TILE_BYTES, "merge buffer");
 
-  // Per key stream: a K tile and a V tile.  The buffer is reused at the end
-  // to hand stream 1's state to stream 0.
-  __shared__ __attribute__((aligned(16))) uint8_t tiles[KS * TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t ring[P * LY::SLOT];
   __shared__ int par[64];
   __shared__ uint64_t masks[64];
 
@@ -379,15 +433,51 @@ void attn_mfma_kernel(AttnArgs a) {
   const int b = u / a.Hkv, gk = u % a.Hkv;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform (scalar)
-  const int ks = wave / W, wr = wave % W;                       // key stream, row wave
-  const int stid = tid - ks * 64 * W;                           // thread within the stream
   const int l16 = lane & 15, g4 = lane >> 4;
-  const int tile0 = (rc * W + wr) * RT;
-  uint16_t* Ks = (uint16_t*)(tiles + ks * TILE_BYTES);
-  uint16_t* Vs = Ks + KT * KSTR;
 
   build_masks(a, b, par, masks);
 
+  const int kb = s * a.chunk, ke = min(a.L, kb + a.chunk);
+  const int ntiles = (ke - kb + KT - 1) / KT;
+  const size_t unit_off = (size_t)u * a.L * D;
+  const uint16_t* kg = (const uint16_t*)a.k + unit_off;
+  const uint16_t* vg = (const uint16_t*)a.v + unit_off;
+
+  if (wave == W) {
+    // ---- loader wave: this lane's key row within a group and 16-byte chunk ----
+    int lj, lc;
+    if constexpr (D == 128) {
+      lj = lane & 3; lc = lane >> 2;
+    } else {
+      const int sg = (lane >> 3) & 1, x = (lane & 7) ^ (4 * sg);
+      lj = 4 * sg + (x & 3); lc = 2 * (lane >> 4) + (x >> 2);
+    }
+    const uint32_t ring_lds =
+        (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)ring;
+    auto issue = [&](int t) SV_INLINE {
+      const int key0 = kb + t * KT + lj;
+      const uint32_t slot = ring_lds + (uint32_t)((t % P) * LY::SLOT);
+#pragma unroll
+      for (int g = 0; g < LY::NG; ++g) {
+        // keys past the end re-read the last row (finite data, masked later)
+        const int key = min(key0 + g * LY::KG, a.L - 1);
+        const uint32_t off = (uint32_t)key * D + 8 * lc;
+        lds_dma16(kg + off, slot + g * LY::GSK);
+        lds_dma16(vg + off, slot + LY::KHALF + g * LY::GSV);
+      }
+    };
+    const int pre = min(RG::AHEAD, ntiles);
+    for (int t = 0; t < pre; ++t) issue(t);
+    for (int j = 0; j < ntiles; ++j) {
+      wait_tiles<LY::NIT, RG::AHEAD - 1>(min(ntiles - 1 - j, RG::AHEAD - 1));
+      ring_barrier();
+      if (j + RG::AHEAD < ntiles) issue(j + RG::AHEAD);
+    }
+    return;
+  }
+
+  // ---- Q fragments (registers for the whole key loop) ----
+  const int tile0 = (rc * W + wave) * RT;
   bf16x8_t qf[RT][KK];
   uint64_t mrow[RT];
   bool live[RT];
@@ -408,81 +498,55 @@ void attn_mfma_kernel(AttnArgs a) {
       mrow[rt] = masks[t];
     }
   }
-  // Q stays in registers for the whole key loop: wait for it here.
-#if SV_SETTLE_MFMA
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) settle(__builtin_bit_cast(u32x4_t, qf[rt][kk]));
-#endif
 
   f32x4_t acc[RT][DT];
-  float m[RT], lpart[RT];
+  float m[RT], lsum[RT];
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) {
     m[rt] = kNegInf;
-    lpart[rt] = 0.f;
+    lsum[rt] = 0.f;
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) acc[rt][dt] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
   }
 
-  // The block's keys [kb, ke) are cut into KS contiguous, tile-aligned parts.
-  const int kb = s * a.chunk, ke = min(a.L, kb + a.chunk);
-  const int ntiles = (ke - kb + KT - 1) / KT;
-  const int tps = (ntiles + KS - 1) / KS;                       // tiles per stream
-  const int sb = min(ke, kb + ks * tps * KT), se = min(ke, sb + tps * KT);
-  const size_t unit_off = (size_t)u * a.L * D;
-  const uint16_t* kg = (const uint16_t*)a.k + unit_off;
-  const uint16_t* vg = (const uint16_t*)a.v + unit_off;
+  // LDS byte offsets of this lane's fragments within a slot.
+  //  K: row 16*sub + l16, chunk 4*kk + g4      -> kofs + sub*KSUB + kk*KKS
+  //  V: keys pv_key(g4, l16/4) and pv_key(g4, 4 + l16/4), bf16 columns
+  //     16*dt + 4*(l16%4) .. +3 (chunk 2*dt + (l16/2)%2, half l16%2)
+  //                                            -> vofs0/vofs1 + dt*VDT
+  int kofs, vofs0, vofs1;
+  constexpr int KSUB = (16 / LY::KG) * LY::GSK;
+  constexpr int KKS = 16 * (LY::chunk_pos(0, 4) - LY::chunk_pos(0, 0));
+  constexpr int VDT = 16 * (LY::chunk_pos(0, 2) - LY::chunk_pos(0, 0));
+  {
+    const int kr = l16;                                   // row within the 16-row half
+    kofs = (kr / LY::KG) * LY::GSK + 16 * LY::chunk_pos(kr % LY::KG, g4);
+    const int vk0 = pv_key(g4, l16 >> 2), vk1 = pv_key(g4, 4 + (l16 >> 2));
+    const int vc = (l16 >> 1) & 1;                        // chunk 0 or 1 of the dt pair
+    vofs0 = LY::KHALF + (vk0 / LY::KG) * LY::GSV + 16 * LY::chunk_pos(vk0 % LY::KG, vc) +
+            8 * (l16 & 1);
+    vofs1 = LY::KHALF + (vk1 / LY::KG) * LY::GSV + 16 * LY::chunk_pos(vk1 % LY::KG, vc) +
+            8 * (l16 & 1);
+  }
+
   const float c = a.scale_log2;
-  const int clean_end = min(a.ctx, se);   // tiles ending here need no mask
-
-  // Register staging: chunk i*64W + stid of the tile, 16 lanes per key row.
-  // Keys past the end are clamped to the last row (finite data, masked later).
-  u32x4_t kreg[NPT], vreg[NPT];
-  auto load_tile = [&](int base) {
-#pragma unroll
-    for (int i = 0; i < NPT; ++i) {
-      const int ch = i * 64 * W + stid;
-      if (NCH % (64 * W) == 0 || (i * W + wr) * 64 < NCH) {   // uniform per wave
-        const int key = min(base + ch / CPR, a.L - 1);
-        const uint32_t off = (uint32_t)(key * D + 8 * (ch % CPR));
-        kreg[i] = *(const u32x4_t*)(kg + off);
-        vreg[i] = *(const u32x4_t*)(vg + off);
-      }
-    }
-  };
-  auto store_tile = [&]() {
-#pragma unroll
-    for (int i = 0; i < NPT; ++i) {
-      const int ch = i * 64 * W + stid;
-      if (NCH % (64 * W) == 0 || (i * W + wr) * 64 < NCH) {
-        const int kr = ch / CPR, kc = ch % CPR;
-        *(u32x4_t*)(Ks + kr * KSTR + 8 * kc) = kreg[i];
-        *(u32x4_t*)(Vs + kr * VSTR + 8 * kc) = vreg[i];
-      }
-    }
+  // tiles [0, nclean) lie wholly inside the prefix: every key visible, no mask
+  const int clean_end = min(a.ctx, ke);
+  const int nclean = clean_end > kb ? (clean_end - kb) / KT : 0;
+  typedef __attribute__((address_space(3))) const uint8_t lds_u8;
+  lds_u8* const ring3 = (lds_u8*)ring;
+  // The slot offset goes through readfirstlane: an opaque wave-uniform value,
+  // so that every fragment address is one base plus an immediate offset.
+  auto slot_of = [&](int t) -> lds_u8* SV_INLINE {
+    return ring3 + __builtin_amdgcn_readfirstlane((t % P) * LY::SLOT);
   };
 
-  // Transposed-read addresses of this lane for V fragment halves: lane j of a
-  // 16-lane group points at V[key(j/4)][16dt + 4(j%4) .. +4]; the hardware
-  // hands lane i the four keys' values at d = 16dt + i.
-  const int vkey0 = pv_key(g4, l16 >> 2), vkey1 = pv_key(g4, 4 + (l16 >> 2));
-  const int vcol = 4 * (l16 & 3);
-
-  if (sb < se) load_tile(sb);
-  // Every stream runs tps iterations so that all waves meet at each barrier.
-  for (int it = 0; it < tps; ++it) {
-    const int base = sb + it * KT;
-    const bool active = base < se;                              // uniform per stream
-    __syncthreads();
-    if (active) store_tile();
-    __syncthreads();
-    if (!active) continue;
-    if (base + KT < se) load_tile(base + KT);
-
-    // S^T for the tile's two 16-key halves.
-    f32x4_t st[RT][2];
+  // S^T for a tile's two 16-key halves.
+  auto qk = [&](lds_u8* slot, f32x4_t (&st)[RT][2]) SV_INLINE {
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) st[rt][0] = st[rt][1] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -490,117 +554,113 @@ void attn_mfma_kernel(AttnArgs a) {
 #pragma unroll
       for (int kk = 0; kk < KK; ++kk) {
         const bf16x8_t kf = __builtin_bit_cast(
-            bf16x8_t, *(const u32x4_t*)(Ks + (16 * sub + l16) * KSTR + 32 * kk + 8 * g4));
+            bf16x8_t, *(__attribute__((address_space(3))) const u32x4_t*)(slot + kofs + sub * KSUB +
+                                                                           kk * KKS));
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt)   // a dead tile (zero Q) computes harmless values
           st[rt][sub] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[rt][kk], st[rt][sub],
                                                                0, 0, 0);
       }
     }
+  };
 
-    // Online softmax in log2 units with a lazily refreshed reference max.
-    const bool clean = base + KT <= clean_end;
-    bf16x8_t pf[RT];
+  // Online softmax of one tile, in log2 units with a lazily raised reference
+  // max m, in two parts.  smax: masks the scores in place (tiles that reach
+  // past the prefix), raises m where the tile's max exceeds it by 2^8 and
+  // rescales the accumulators of those rows (rare).  sexp: probabilities as
+  // bf16 in the B-operand layout of P.V (pf), their rounded sum into lsum.
+  auto smax = [&](auto clean_tag, f32x4_t (&st)[RT][2], int base) SV_INLINE {
+    constexpr bool CLEAN = decltype(clean_tag)::value;
+    float mold[RT];
+    bool raised = false;
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) {
-      float sc[8];
-#pragma unroll
-      for (int sub = 0; sub < 2; ++sub)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) sc[4 * sub + r] = st[rt][sub][r];
-      if (!clean) {
+      if constexpr (!CLEAN) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const int key = base + (e < 4 ? 4 * g4 + e : 16 + 4 * g4 + e - 4);
-          if (!(key < se && tail_visible(mrow[rt], key, a.ctx))) sc[e] = kNegInf;
+          if (!(key < ke && tail_visible(mrow[rt], key, a.ctx))) st[rt][e >> 2][e & 3] = kNegInf;
         }
       }
-      float mt = sc[0];
+      const f32x4_t x0 = st[rt][0], x1 = st[rt][1];
+      float mt = fmaxf(fmaxf(fmaxf(x0[0], x0[1]), fmaxf(x0[2], x0[3])),
+                       fmaxf(fmaxf(x1[0], x1[1]), fmaxf(x1[2], x1[3])));
+      mt = group4_max(mt) * c;                  // scale > 0: max commutes with scaling
+      mold[rt] = m[rt];
+      if (mt > m[rt] + kRescaleLog2) m[rt] = mt;
+      raised |= m[rt] != mold[rt];
+    }
+    if (__any(raised)) {
 #pragma unroll
-      for (int e = 1; e < 8; ++e) mt = fmaxf(mt, sc[e]);
-      mt = fmaxf(mt, __shfl_xor(mt, 16));
-      mt = fmaxf(mt, __shfl_xor(mt, 32));
-      mt *= c;                                  // scale > 0: max commutes with scaling
-      const bool bump = mt > m[rt] + kRescaleLog2;
-      if (__any(bump)) {
-        // lanes that keep their reference (possibly -inf) must not compute -inf - -inf
-        const float alpha = bump ? fast_exp2(m[rt] - mt) : 1.f;   // m = -inf: 0
-        if (bump) m[rt] = mt;
-        lpart[rt] *= alpha;
+      for (int rt = 0; rt < RT; ++rt) {
+        // unchanged rows (possibly still -inf) keep factor 1; mold = -inf gives 0
+        const float alpha = m[rt] == mold[rt] ? 1.f : fast_exp2(mold[rt] - m[rt]);
+        lsum[rt] *= alpha;
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt) acc[rt][dt] *= alpha;
       }
-      const float msafe = (m[rt] == kNegInf) ? 0.f : m[rt];
-      float ps = 0.f;
+    }
+  };
+  const bf16x2_t ones = {(__bf16)1.f, (__bf16)1.f};
+  auto sexp = [&](auto clean_tag, const f32x4_t (&st)[RT][2], bf16x8_t (&pf)[RT]) SV_INLINE {
+    constexpr bool CLEAN = decltype(clean_tag)::value;
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+      // a tile without visible keys leaves m = -inf: subtract 0 then (p = 0)
+      const float msub = CLEAN ? m[rt] : (m[rt] == kNegInf ? 0.f : m[rt]);
+      const f32x4_t x0 = st[rt][0], x1 = st[rt][1];
+      const float sc[8] = {x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
       bf16x2_t pk[4];
+      float sum = 0.f;
 #pragma unroll
       for (int e = 0; e < 8; e += 2) {
-        const float p0 = fast_exp2(fmaf(sc[e], c, -msafe));
-        const float p1 = fast_exp2(fmaf(sc[e + 1], c, -msafe));
-        ps += p0 + p1;
+        const float p0 = fast_exp2(fmaf(sc[e], c, -msub));
+        const float p1 = fast_exp2(fmaf(sc[e + 1], c, -msub));
         pk[e / 2] = __builtin_convertvector((f32x2_t){p0, p1}, bf16x2_t);
+        sum = __builtin_amdgcn_fdot2_f32_bf16(pk[e / 2], ones, sum, false);
       }
-      lpart[rt] += ps;
+      lsum[rt] += sum;
       pf[rt] = __builtin_shufflevector(__builtin_shufflevector(pk[0], pk[1], 0, 1, 2, 3),
                                        __builtin_shufflevector(pk[2], pk[3], 0, 1, 2, 3),
                                        0, 1, 2, 3, 4, 5, 6, 7);
     }
+  };
 
-    // O^T += V^T P^T.
+  // O^T += V^T P^T.
+  auto pv = [&](lds_u8* slot, const bf16x8_t (&pf)[RT]) SV_INLINE {
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
       const s16x4_t v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (__attribute__((address_space(3))) s16x4_t*)(Vs + vkey0 * VSTR + 16 * dt + vcol));
+          (__attribute__((address_space(3))) s16x4_t*)(slot + vofs0 + dt * VDT));
       const s16x4_t v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-          (__attribute__((address_space(3))) s16x4_t*)(Vs + vkey1 * VSTR + 16 * dt + vcol));
+          (__attribute__((address_space(3))) s16x4_t*)(slot + vofs1 + dt * VDT));
       const bf16x8_t vf = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(v0, v1, 0, 1, 2, 3,
                                                                                4, 5, 6, 7));
 #pragma unroll
       for (int rt = 0; rt < RT; ++rt)
         acc[rt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf[rt], acc[rt][dt], 0, 0, 0);
     }
-  }
+  };
+
+  const std::integral_constant<bool, true> kClean;
+  const std::integral_constant<bool, false> kMasked;
+  auto step = [&](auto clean_tag, int it) SV_INLINE {
+    ring_barrier();                             // tile it has landed in its slot
+    f32x4_t st[RT][2];
+    bf16x8_t pf[RT];
+    qk(slot_of(it), st);
+    smax(clean_tag, st, kb + it * KT);
+    sexp(clean_tag, st, pf);
+    pv(slot_of(it), pf);
+  };
+  int it = 0;
+  for (; it < ntiles && it < nclean; ++it) step(kClean, it);
+  for (; it < ntiles; ++it) step(kMasked, it);
 
   // Row sums over the four lane groups (every lane of a row gets the total).
   float lt[RT];
 #pragma unroll
-  for (int rt = 0; rt < RT; ++rt) {
-    lt[rt] = lpart[rt];
-    lt[rt] += __shfl_xor(lt[rt], 16);
-    lt[rt] += __shfl_xor(lt[rt], 32);
-  }
-
-  if constexpr (KS == 2) {
-    // Stream 1 hands its state to stream 0 through LDS (same row wave, same
-    // lane, same layout), and stream 0 merges the two.
-    __syncthreads();
-    f32x4_t* xo = (f32x4_t*)tiles;
-    float* xm = (float*)(tiles + W * RT * DT * 64 * 16);
-    if (ks == 1) {
-#pragma unroll
-      for (int rt = 0; rt < RT; ++rt) {
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt) xo[((wr * RT + rt) * DT + dt) * 64 + lane] = acc[rt][dt];
-        xm[((wr * RT + rt) * 64 + lane) * 2] = m[rt];
-        xm[((wr * RT + rt) * 64 + lane) * 2 + 1] = lt[rt];
-      }
-    }
-    __syncthreads();
-    if (ks == 1) return;
-#pragma unroll
-    for (int rt = 0; rt < RT; ++rt) {
-      const float m2 = xm[((wr * RT + rt) * 64 + lane) * 2];
-      const float l2 = xm[((wr * RT + rt) * 64 + lane) * 2 + 1];
-      const float mx = fmaxf(m[rt], m2);
-      if (mx == kNegInf) continue;
-      const float a1 = fast_exp2(m[rt] - mx), a2 = fast_exp2(m2 - mx);
-      lt[rt] = lt[rt] * a1 + l2 * a2;
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt)
-        acc[rt][dt] = acc[rt][dt] * a1 + xo[((wr * RT + rt) * DT + dt) * 64 + lane] * a2;
-      m[rt] = mx;
-    }
-  }
+  for (int rt = 0; rt < RT; ++rt) lt[rt] = group4_sum(lsum[rt]);
 
   // Lane holds O^T[16dt + 4g4 + r][row l16]: the final output when the block
   // saw every key (one split), else an unnormalised partial (o, m, l).
@@ -652,19 +712,23 @@ __global__ __launch_bounds__(128) void attn_combine_kernel(AttnArgs a) {
 template <int D, int RT>
 static void launch_mfma_w(const AttnPlan& p, const AttnArgs& a, hipStream_t st, dim3 grid) {
   switch (p.waves) {
-    case 1: attn_mfma_kernel<D, RT, 1, 1><<<grid, 64, 0, st>>>(a); break;
-    case 2: attn_mfma_kernel<D, RT, 2, 1><<<grid, 128, 0, st>>>(a); break;
-    case 3: attn_mfma_kernel<D, RT, 3, 1><<<grid, 192, 0, st>>>(a); break;
-    case 4: attn_mfma_kernel<D, RT, 4, 1><<<grid, 256, 0, st>>>(a); break;
-    case 5: attn_mfma_kernel<D, RT, 5, 1><<<grid, 320, 0, st>>>(a); break;
-    case 6: attn_mfma_kernel<D, RT, 6, 1><<<grid, 384, 0, st>>>(a); break;
-    case 7: attn_mfma_kernel<D, RT, 7, 1><<<grid, 448, 0, st>>>(a); break;
-    default: attn_mfma_kernel<D, RT, 8, 1><<<grid, 512, 0, st>>>(a); break;
+    // W compute waves + the loader wave
+    case 1: attn_mfma_kernel<D, RT, 1><<<grid, 128, 0, st>>>(a); break;
+    case 2: attn_mfma_kernel<D, RT, 2><<<grid, 192, 0, st>>>(a); break;
+    case 3: attn_mfma_kernel<D, RT, 3><<<grid, 256, 0, st>>>(a); break;
+    case 4: attn_mfma_kernel<D, RT, 4><<<grid, 320, 0, st>>>(a); break;
+    case 5: attn_mfma_kernel<D, RT, 5><<<grid, 384, 0, st>>>(a); break;
+    case 6: attn_mfma_kernel<D, RT, 6><<<grid, 448, 0, st>>>(a); break;
+    case 7: attn_mfma_kernel<D, RT, 7><<<grid, 512, 0, st>>>(a); break;
+    default:
+      // three row tiles need more than the 168 registers that 9 waves per CU allow
+      if constexpr (RT < 3) attn_mfma_kernel<D, RT, 8><<<grid, 576, 0, st>>>(a);
+      break;
   }
 }
 
-template <int D, int KS>
-static void launch_mfma_rt(const AttnPlan& p, const AttnArgs& a, hipStream_t st, dim3 grid) {
+template <int D>
+static void launch_mfma(const AttnPlan& p, const AttnArgs& a, hipStream_t st, dim3 grid) {
   switch (p.rt) {
     case 1: launch_mfma_w<D, 1>(p, a, st, grid); break;
     case 2: launch_mfma_w<D, 2>(p, a, st, grid); break;
@@ -673,35 +737,24 @@ static void launch_mfma_rt(const AttnPlan& p, const AttnArgs& a, hipStream_t st,
 }
 
 template <int D>
-static void launch_mfma(const AttnPlan& p, const AttnArgs& a, hipStream_t st, dim3 grid) {
-  // two key streams are planned only with one row tile per wave and <= 4 row waves
-  if (p.kstreams == 2) {
-    switch (p.waves) {
-      case 1: attn_mfma_kernel<D, 1, 1, 2><<<grid, 128, 0, st>>>(a); break;
-      case 2: attn_mfma_kernel<D, 1, 2, 2><<<grid, 256, 0, st>>>(a); break;
-      case 3: attn_mfma_kernel<D, 1, 3, 2><<<grid, 384, 0, st>>>(a); break;
-      default: attn_mfma_kernel<D, 1, 4, 2><<<grid, 512, 0, st>>>(a); break;
-    }
-  } else {
-    launch_mfma_rt<D, 1>(p, a, st, grid);
-  }
-}
-
-template <typename TIn, int D>
 static void launch_valu(const AttnPlan& p, const AttnArgs& a, hipStream_t st, dim3 grid) {
   switch (p.rmax) {
-    case 1: attn_valu_kernel<TIn, D, 1><<<grid, 256, 0, st>>>(a); break;
-    case 2: attn_valu_kernel<TIn, D, 2><<<grid, 256, 0, st>>>(a); break;
-    case 4: attn_valu_kernel<TIn, D, 4><<<grid, 256, 0, st>>>(a); break;
-    default: attn_valu_kernel<TIn, D, 8><<<grid, 256, 0, st>>>(a); break;
+    case 1: attn_valu_kernel<D, 1><<<grid, 256, 0, st>>>(a); break;
+    case 2: attn_valu_kernel<D, 2><<<grid, 256, 0, st>>>(a); break;
+    case 4: attn_valu_kernel<D, 4><<<grid, 256, 0, st>>>(a); break;
+    default: attn_valu_kernel<D, 8><<<grid, 256, 0, st>>>(a); break;
   }
 }
 
 // Splits and tiles for a problem; a pure function of the shape so that the
 // workspace query and the launch always agree.  The block targets aim at one
-// full wave of resident blocks on the 256 CUs.
+// full wave of resident blocks on the 256 CUs: the MFMA kernel's LDS ring
+// admits two blocks per CU with one row tile per wave, one block otherwise.
+#ifndef SV_MFMA_BLOCKS_RT1
+#define SV_MFMA_BLOCKS_RT1 512
+#endif
 #ifndef SV_MFMA_BLOCKS
-#define SV_MFMA_BLOCKS 1024
+#define SV_MFMA_BLOCKS 256
 #endif
 #ifndef SV_VALU_BLOCKS
 #define SV_VALU_BLOCKS 512
@@ -709,28 +762,26 @@ static void launch_valu(const AttnPlan& p, const AttnArgs& a, hipStream_t st, di
 #ifndef SV_MIN_CHUNK
 #define SV_MIN_CHUNK 256
 #endif
-#ifndef SV_FUSE_UNITS
-#define SV_FUSE_UNITS 512
-#endif
 AttnPlan plan_attention(int B, int T, int Hq, int Hkv, int D, int ctx, int bf16) {
   AttnPlan p{};
   const int G = Hq / Hkv, R = G * T, L = ctx + T, units = B * Hkv;
   p.rows = R;
-  p.mfma = bf16 && R >= 16;
+  // bf16 always takes the MFMA kernel (fewer than 16 rows leave part of the
+  // one row tile empty: the pass is bound by the K/V stream, not the matrix
+  // unit); fp32 inputs take the VALU kernel.
+  p.mfma = bf16;
   int tile, blocks_target;
   if (p.mfma) {
     const int tiles = (R + 15) / 16;
-    // one to three 16-row tiles per wave, at most 8 waves; the rest in row chunks
+    // one to three 16-row tiles per wave, at most 8 compute waves (7 with three
+    // tiles each); the rest in row chunks
     p.rt = tiles <= 8 ? 1 : tiles <= 16 ? 2 : 3;
+    const int max_waves = p.rt == 3 ? 7 : 8;
     int waves = (tiles + p.rt - 1) / p.rt;
-    p.row_chunks = (waves + 7) / 8;
+    p.row_chunks = (waves + max_waves - 1) / max_waves;
     p.waves = (waves + p.row_chunks - 1) / p.row_chunks;
-    // With enough (sequence, KV head) units to fill the chip, one block holds
-    // two key streams and merges them itself: one launch, no partials.
-    p.kstreams = 1;
-    if (p.waves <= 4 && units * p.row_chunks >= SV_FUSE_UNITS) p.kstreams = 2;
     tile = kMfmaKeys;
-    blocks_target = SV_MFMA_BLOCKS;
+    blocks_target = p.rt == 1 ? SV_MFMA_BLOCKS_RT1 : SV_MFMA_BLOCKS;
   } else {
     const int rr = R < 8 ? R : 8;
     p.rmax = rr <= 1 ? 1 : rr <= 2 ? 2 : rr <= 4 ? 4 : 8;
@@ -741,7 +792,6 @@ AttnPlan plan_attention(int B, int T, int Hq, int Hkv, int D, int ctx, int bf16)
   }
   const int min_chunk = SV_MIN_CHUNK;
   int S = (blocks_target + units * p.row_chunks - 1) / (units * p.row_chunks);
-  if (p.mfma && p.kstreams == 2) S = 1;
   const int s_max = (L + min_chunk - 1) / min_chunk;
   if (S > s_max) S = s_max;
   if (S < 1) S = 1;
@@ -771,12 +821,9 @@ hipError_t launch_attention(const AttnPlan& p, const void* q, const void* k, con
   if (p.mfma) {
     if (D == 64) launch_mfma<64>(p, a, st, grid);
     else launch_mfma<128>(p, a, st, grid);
-  } else if (bf16) {
-    if (D == 64) launch_valu<uint16_t, 64>(p, a, st, grid);
-    else launch_valu<uint16_t, 128>(p, a, st, grid);
   } else {
-    if (D == 64) launch_valu<float, 64>(p, a, st, grid);
-    else launch_valu<float, 128>(p, a, st, grid);
+    if (D == 64) launch_valu<64>(p, a, st, grid);
+    else launch_valu<128>(p, a, st, grid);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || (p.mfma && p.splits == 1)) return e;

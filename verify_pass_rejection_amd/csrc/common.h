@@ -44,8 +44,7 @@ struct AttnPlan {
   int rows;        // R = G * T grouped rows per KV head
   int rmax;        // VALU: rows handled per block (1, 2, 4 or 8)
   int rt;          // MFMA: 16-row tiles per wave (1..4)
-  int waves;       // waves per block (per key stream for the MFMA kernel)
-  int kstreams;    // MFMA: key streams per block (1 or 2)
+  int waves;       // waves per block (MFMA: compute waves, plus one loader wave)
   int row_chunks;  // blocks along the row axis
   int splits;      // S: key-range splits per (sequence, KV head)
   int chunk;       // keys per split (multiple of the kernel's key tile)
