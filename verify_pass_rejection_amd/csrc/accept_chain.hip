@@ -7,16 +7,15 @@
 // pure target sampling.  The pass gives N+1 target distributions, so when all
 // N drafts are kept the last one supplies a bonus token.
 //
-// Four kernels (kernel boundaries order every step; no in-kernel signalling):
+// Three kernels (kernel boundaries order every step; no in-kernel signalling):
 //  chain_stats  — one pass over every logit row (all B*(2N+1) rows), per chunk
 //                 the row maximum and sum of 2^((z - max) log2(e)/tau);
-//  chain_decide — one block per sequence: merges the chunk statistics into
-//                 the row normalisers, runs the N ratio tests (two gathers a
-//                 row), takes the first rejection k and records the normalisers
-//                 of the row(s) to draw from;
-//  chain_chunks — grid (vocabulary chunk, sequence): every block sums the
-//                 weights of its chunk of the drawn row (the residual
-//                 (p_k - q_k)+, or p_N);
+//  chain_chunks — grid (vocabulary chunk, sequence): every block first takes
+//                 the sequence's decision (merges the chunk statistics into
+//                 the row normalisers, runs the N ratio tests with two gathers
+//                 a row, takes the first rejection k), then sums the weights
+//                 of its chunk of the drawn row (the residual (p_k - q_k)+, or
+//                 p_N); block 0 records the decision;
 //  chain_select — one block per sequence: locates the chunk holding the
 //                 inverse-CDF crossing from the chunk sums and re-scans that
 //                 one chunk (if the residual is empty it first sums p_k's
@@ -48,10 +47,10 @@ struct ChainArgs {
 };
 
 #ifndef SV_STATS_THREADS
-#define SV_STATS_THREADS 256
+#define SV_STATS_THREADS 512
 #endif
 #ifndef SV_STATS_CHUNK
-#define SV_STATS_CHUNK 8192
+#define SV_STATS_CHUNK 16384
 #endif
 constexpr int kStatsThreads = SV_STATS_THREADS;
 constexpr int kStatsChunk = SV_STATS_CHUNK;   // logits per stats block
@@ -61,10 +60,41 @@ constexpr int kStatsChunk = SV_STATS_CHUNK;   // logits per stats block
 constexpr int kDrawThreads = 1024;
 constexpr int kDrawPer = SV_DRAW_PER; // weights per thread per draw chunk
 constexpr int kDrawChunk = kDrawThreads * kDrawPer;
+#ifndef SV_DRAW_CPB
+#define SV_DRAW_CPB 3
+#endif
+constexpr int kDrawCpb = SV_DRAW_CPB;  // draw chunks summed per chain_chunks block
 
 __device__ __forceinline__ const float* chain_row(const ChainArgs& a, int b, int rho) {
   return rho <= a.N ? a.target + ((size_t)b * (a.N + 1) + rho) * a.V
                     : a.draft + ((size_t)b * a.N + (rho - a.N - 1)) * a.V;
+}
+
+#ifndef SV_STATS_NT
+#define SV_STATS_NT 1
+#endif
+// Logits are read once by the statistics pass.
+__device__ __forceinline__ float4 load_stream4(const float* p) {
+#if SV_STATS_NT
+  typedef float f32x4_nt __attribute__((ext_vector_type(4)));
+  const f32x4_nt v = __builtin_nontemporal_load((const f32x4_nt*)p);
+  return make_float4(v[0], v[1], v[2], v[3]);
+#else
+  return *(const float4*)p;
+#endif
+}
+
+#ifndef SV_DRAW_NT
+#define SV_DRAW_NT 0
+#endif
+__device__ __forceinline__ float4 load_draw4(const float* p) {
+#if SV_DRAW_NT
+  typedef float f32x4_nt __attribute__((ext_vector_type(4)));
+  const f32x4_nt v = __builtin_nontemporal_load((const f32x4_nt*)p);
+  return make_float4(v[0], v[1], v[2], v[3]);
+#else
+  return *(const float4*)p;
+#endif
 }
 
 // (m, s) pairs: s = sum 2^((z - m) c).
@@ -91,7 +121,7 @@ __global__ __launch_bounds__(kStatsThreads) void chain_stats_kernel(ChainArgs a)
     const int j = begin + (it * kStatsThreads + threadIdx.x) * VEC;
     if constexpr (VEC == 4) {
       float4 x = {kNegInf, kNegInf, kNegInf, kNegInf};
-      if (j < a.V) x = *(const float4*)(z + j);   // V % 4 == 0 on this path
+      if (j < a.V) x = load_stream4(z + j);   // V % 4 == 0 on this path
       v[it * 4 + 0] = x.x; v[it * 4 + 1] = x.y; v[it * 4 + 2] = x.z; v[it * 4 + 3] = x.w;
     } else {
       v[it] = j < a.V ? z[j] : kNegInf;
@@ -146,8 +176,8 @@ __device__ __forceinline__ void draw_weights(const DrawRow& r, int V, int chunk,
     for (int i = 0; i < kDrawPer; i += 4) {
       float4 p4 = {kNegInf, kNegInf, kNegInf, kNegInf}, q4 = p4;
       if (j0 + i < V) {                 // V % 4 == 0 on this path: all four in range
-        p4 = *(const float4*)(r.zp + j0 + i);
-        if (r.zq) q4 = *(const float4*)(r.zq + j0 + i);
+        p4 = load_draw4(r.zp + j0 + i);
+        if (r.zq) q4 = load_draw4(r.zq + j0 + i);
       }
       xp[i] = p4.x; xp[i + 1] = p4.y; xp[i + 2] = p4.z; xp[i + 3] = p4.w;
       xq[i] = q4.x; xq[i + 1] = q4.y; xq[i + 2] = q4.z; xq[i + 3] = q4.w;
@@ -196,13 +226,16 @@ __device__ __forceinline__ void chunk_scan(const float* w, float* prefix, float*
   for (int e = 0; e < kDrawPer; ++e) prefix[e] = off + local[e];
 }
 
-__global__ __launch_bounds__(256) void chain_decide_kernel(ChainArgs a) {
-  __shared__ float row_m[128], row_l[128];     // per row: max, log2(sum)
-  __shared__ int keep[64];
-  const int b = blockIdx.x, tid = threadIdx.x;
-  const int N = a.N, rows = 2 * N + 1;
+// The decision of sequence b, taken by a whole block of NT threads: merges the
+// chunk statistics into the row normalisers (row_m: max, row_l: log2 of the
+// sum; one wave per row, lane-strided partial merges then a butterfly, a
+// fixed order), runs the N ratio tests (keep x_i iff u < p_i(x_i)/q_i(x_i))
+// and returns k, the first rejection (N if none), to every thread.
+template <int NT>
+__device__ __forceinline__ int chain_decision(const ChainArgs& a, int b, float* row_m,
+                                              float* row_l, int* keep, int* s_k) {
+  const int tid = threadIdx.x, N = a.N, rows = 2 * N + 1;
   const int lane = tid & 63, wave = tid >> 6;
-
   // The drafted tokens' logits are gathered first so that their latency
   // overlaps the merge of the chunk statistics.
   int x = -1;
@@ -214,10 +247,7 @@ __global__ __launch_bounds__(256) void chain_decide_kernel(ChainArgs a) {
       zq = a.draft[((size_t)b * N + tid) * a.V + x];
     }
   }
-
-  // Row normalisers: one wave per row merges the row's chunk statistics in a
-  // fixed tree order (lane-strided partial merges, then a butterfly).
-  for (int r = wave; r < rows; r += 4) {
+  for (int r = wave; r < rows; r += NT / kWave) {
     const float2* st = a.stats + ((size_t)b * rows + r) * a.nchunks;
     float M = kNegInf, S = 0.f;
     for (int i = lane; i < a.nchunks; i += kWave) merge_ms(M, S, st[i].x, st[i].y, a.c2);
@@ -229,8 +259,6 @@ __global__ __launch_bounds__(256) void chain_decide_kernel(ChainArgs a) {
     if (lane == 0) { row_m[r] = M; row_l[r] = log2f(S); }
   }
   __syncthreads();
-
-  // Ratio tests: keep x_i iff u < p_i(x_i)/q_i(x_i).
   if (tid < N) {
     bool ok = false;
     if (x >= 0 && x < a.V) {
@@ -246,10 +274,10 @@ __global__ __launch_bounds__(256) void chain_decide_kernel(ChainArgs a) {
     int k = N;
     for (int i = 0; i < N; ++i)
       if (!keep[i]) { k = i; break; }
-    const float mq = k < N ? row_m[N + 1 + k] : 0.f, lq = k < N ? row_l[N + 1 + k] : 0.f;
-    a.decision[b] = make_float4(__int_as_float(k), row_m[k], row_l[k], 0.f);
-    a.decision_q[b] = make_float4(mq, lq, 0.f, 0.f);
+    *s_k = k;
   }
+  __syncthreads();
+  return *s_k;
 }
 
 // The drawn row's weights for sequence b, from the decision record.
@@ -272,17 +300,46 @@ __device__ __forceinline__ void draw_rows(const ChainArgs& a, int b, int& k, Dra
   }
 }
 
+// Every block of a sequence takes the decision itself (the statistics are
+// small), so that no launch sits between the statistics and the draw, and
+// then sums kDrawCpb chunks of the drawn row; block 0 records the decision
+// for chain_select.
 template <int VEC>
 __global__ __launch_bounds__(kDrawThreads) void chain_chunks_kernel(ChainArgs a) {
   __shared__ float wave_tot[kDrawThreads / kWave], wave_off[kDrawThreads / kWave];
-  const int c = blockIdx.x, b = blockIdx.y, nch = a.dchunks;
-  int k;
-  DrawRow dp, dr;
-  draw_rows(a, b, k, dp, dr);
-  float w[kDrawPer], pre[kDrawPer];
-  draw_weights<VEC>(dr, a.V, c, w);
-  chunk_scan(w, pre, wave_tot, wave_off);
-  if (threadIdx.x == kDrawThreads - 1) a.csum[(size_t)b * 2 * nch + c] = pre[kDrawPer - 1];
+  __shared__ float row_m[128], row_l[128];
+  __shared__ int keep[64], s_k;
+  const int c = blockIdx.x, b = blockIdx.y, nch = a.dchunks, N = a.N;
+  const int k = chain_decision<kDrawThreads>(a, b, row_m, row_l, keep, &s_k);
+  DrawRow dr;
+  dr.zp = a.target + ((size_t)b * (N + 1) + k) * a.V;
+  dr.mp = row_m[k];
+  dr.lp = row_l[k];
+  dr.c = a.c2;
+  dr.zq = nullptr;
+  dr.mq = dr.lq = 0.f;
+  if (k < N) {
+    dr.zq = a.draft + ((size_t)b * N + k) * a.V;
+    dr.mq = row_m[N + 1 + k];
+    dr.lq = row_l[N + 1 + k];
+  }
+  if (c == 0 && threadIdx.x == 0) {
+    a.decision[b] = make_float4(__int_as_float(k), row_m[k], row_l[k], 0.f);
+    a.decision_q[b] = make_float4(dr.mq, dr.lq, 0.f, 0.f);
+  }
+  // This block's kDrawCpb chunks: every load first, then one scan per chunk
+  // (chunks past the row have zero weights and are not written).
+  float w[kDrawCpb][kDrawPer];
+#pragma unroll
+  for (int cc = 0; cc < kDrawCpb; ++cc) draw_weights<VEC>(dr, a.V, c * kDrawCpb + cc, w[cc]);
+#pragma unroll
+  for (int cc = 0; cc < kDrawCpb; ++cc) {
+    const int ch = c * kDrawCpb + cc;
+    if (ch >= nch) break;
+    float pre[kDrawPer];
+    chunk_scan(w[cc], pre, wave_tot, wave_off);
+    if (threadIdx.x == kDrawThreads - 1) a.csum[(size_t)b * 2 * nch + ch] = pre[kDrawPer - 1];
+  }
 }
 
 template <int VEC>
@@ -430,10 +487,7 @@ hipError_t launch_chain(const ChainPlan& p, const float* target, const float* dr
   else chain_stats_kernel<1><<<g1, kStatsThreads, 0, st>>>(a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  chain_decide_kernel<<<B, 256, 0, st>>>(a);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  const dim3 g2(p.dchunks, B);
+  const dim3 g2((p.dchunks + kDrawCpb - 1) / kDrawCpb, B);
   if (vec4) chain_chunks_kernel<4><<<g2, kDrawThreads, 0, st>>>(a);
   else chain_chunks_kernel<1><<<g2, kDrawThreads, 0, st>>>(a);
   e = hipGetLastError();

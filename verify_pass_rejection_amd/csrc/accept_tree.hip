@@ -11,10 +11,11 @@
 //  tree_argmax — every node's logit row is read once; per chunk the maximum
 //                and its lowest index;
 //  tree_walk   — one wave per sequence: merges the chunks into the target's
-//                choice a_i at each node, then walks the (topologically
-//                ordered) parents: node i is accepted iff its parent is and its
-//                token equals a_parent(i); the deepest accepted node (lowest id
-//                on ties) ends the path; a_l follows the path's tokens.
+//                choice a_i at each node; every node then walks up its
+//                parents: node i is accepted iff each node on its way to the
+//                root carries its parent's choice; the deepest accepted node
+//                (lowest id on ties, a wave reduction) ends the path; a_l
+//                follows the path's tokens.
 
 #include "common.h"
 
@@ -37,6 +38,8 @@ struct TreeArgs {
 constexpr int kArgThreads = 256;
 constexpr int kArgChunk = 8192;
 
+typedef float f32x4_nt __attribute__((ext_vector_type(4)));
+
 // (v, i) is better than (bv, bi): larger value, or equal value and lower index.
 __device__ __forceinline__ bool better(float v, int i, float bv, int bi) {
   return v > bv || (v == bv && i < bi);
@@ -57,7 +60,10 @@ __global__ __launch_bounds__(kArgThreads) void tree_argmax_kernel(TreeArgs a) {
     const int j = begin + (it * kArgThreads + threadIdx.x) * VEC;
     if constexpr (VEC == 4) {
       float4 x = {kNegInf, kNegInf, kNegInf, kNegInf};
-      if (j < a.V) x = *(const float4*)(z + j);
+      if (j < a.V) {                      // logits are read once: non-temporal
+        const f32x4_nt y = __builtin_nontemporal_load((const f32x4_nt*)(z + j));
+        x = make_float4(y[0], y[1], y[2], y[3]);
+      }
       v[it * 4 + 0] = x.x; v[it * 4 + 1] = x.y; v[it * 4 + 2] = x.z; v[it * 4 + 3] = x.w;
     } else {
       v[it] = j < a.V ? z[j] : kNegInf;
@@ -90,7 +96,7 @@ __global__ __launch_bounds__(kArgThreads) void tree_argmax_kernel(TreeArgs a) {
 }
 
 __global__ __launch_bounds__(64) void tree_walk_kernel(TreeArgs a) {
-  __shared__ int choice[64], par[64], tok[64], depth[64], acc[64], path_nodes[64];
+  __shared__ int choice[64], par[64], tok[64], path_nodes[64];
   __shared__ int s_best, s_depth;
   const int b = blockIdx.x, i = threadIdx.x, T = a.T;
   if (i < T) {
@@ -107,22 +113,34 @@ __global__ __launch_bounds__(64) void tree_walk_kernel(TreeArgs a) {
     tok[i] = a.tokens[row];
   }
   __syncthreads();
-  if (i == 0) {
-    depth[0] = 0;
-    acc[0] = 1;
-    int best = 0;
-    for (int n = 1; n < T; ++n) {
+  // Every node walks up to the root on its own: accepted iff each node on the
+  // way carries its parent's choice; a parent that is not strictly smaller
+  // (malformed input) ends the walk unaccepted.
+  int depth = -1;                                // -1: not accepted
+  if (i < T) {
+    bool ok = true;
+    int d = 0, n = i;
+    while (n != 0) {
       const int p = par[n];
-      if (p < 0 || p >= n) { depth[n] = 0; acc[n] = 0; continue; }
-      depth[n] = depth[p] + 1;
-      acc[n] = acc[p] && tok[n] == choice[p];
-      if (acc[n] && depth[n] > depth[best]) best = n;
+      if (p < 0 || p >= n) { ok = false; break; }
+      ok = ok && tok[n] == choice[p];
+      n = p;
+      ++d;
     }
-    const int d = depth[best];
-    int n = best;
-    for (int k = d; k >= 0; --k) { path_nodes[k] = n; n = par[n]; }
-    s_best = best;
-    s_depth = d;
+    if (ok) depth = d;
+  }
+  // Deepest accepted node, lowest id on ties (node 0 is always accepted).
+  int best_d = depth, best_i = i;
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) {
+    const int od = __shfl_xor(best_d, off), oi = __shfl_xor(best_i, off);
+    if (od > best_d || (od == best_d && oi < best_i)) { best_d = od; best_i = oi; }
+  }
+  if (i == 0) {
+    int n = best_i;
+    for (int k = best_d; k >= 0; --k) { path_nodes[k] = n; n = par[n]; }
+    s_best = best_i;
+    s_depth = best_d;
   }
   __syncthreads();
   if (i < T) {

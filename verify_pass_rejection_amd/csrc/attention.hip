@@ -390,9 +390,17 @@ struct MfmaRing {
 
 // One direct load of 16 bytes per lane into LDS at byte offset lds (wave-
 // uniform; lane L writes lds + 16L).  M0 carries the LDS address; the nop
-// covers the M0-write to LDS-DMA hazard.
+// covers the M0-write to LDS-DMA hazard.  K and V are read once: SV_KV_NT
+// marks the loads non-temporal.
+#ifndef SV_KV_NT
+#define SV_KV_NT 1
+#endif
 __device__ __forceinline__ void lds_dma16(const void* g, uint32_t lds) {
+#if SV_KV_NT
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off nt" ::"v"(g), "{m0}"(lds) : "memory");
+#else
   asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "{m0}"(lds) : "memory");
+#endif
 }
 template <int N>
 __device__ __forceinline__ void wait_vm() {
