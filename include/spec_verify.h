@@ -90,7 +90,8 @@ const char* spec_status_string(spec_status status);
  *   out      [B, T, Hq, D] float32
  *   scale    softmax scale, normally 1/sqrt(D); must be finite and > 0
  *
- * Limits: 1 <= T <= 64, D in {64, 128}, Hkv >= 1, Hq % Hkv == 0, ctx >= 0.
+ * Limits: 1 <= T <= 64, D in {64, 128}, Hkv >= 1, Hq % Hkv == 0, ctx >= 0;
+ * q, k, v and out 16-byte aligned (SPEC_ERR_UNSUPPORTED otherwise).
  * ------------------------------------------------------------------------- */
 size_t spec_verify_attention_workspace(int B, int T, int Hq, int Hkv, int D, int ctx,
                                        spec_dtype dtype);

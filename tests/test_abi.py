@@ -65,6 +65,8 @@ def test_attention_validation():
     assert attn(scale=0.0) == SHAPE
     assert attn(scale=-0.5) == SHAPE
     assert attn(ws_bytes=16) == WS
+    assert attn(q=FAKE + 4) == UNSUP         # 16-byte loads and stores need alignment
+    assert attn(out=FAKE + 8) == UNSUP
     assert attn(B=0, q=None) == OK          # empty problem: nothing launched
     assert attn(T=0, q=None) == OK
 

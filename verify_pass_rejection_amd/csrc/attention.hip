@@ -693,25 +693,54 @@ void attn_mfma_kernel(AttnArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Split combine: block per (row, unit), one thread per d.
+// Split combine: log-sum-exp merge of the S partials of each row.  A block
+// of 256 threads takes 1024/D rows of one unit, D/4 threads per row, each
+// thread a float4 of the output; the split weights 2^(m_s - max) are computed
+// once per row into LDS.  Grid (ceil(R / rows per block), units).
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(128) void attn_combine_kernel(AttnArgs a) {
-  const int row = blockIdx.x, u = blockIdx.y, d = threadIdx.x;
+constexpr int kCombineThreads = 256;
+constexpr int kCombineMaxS = 512;            // >= every split count the planner makes
+
+template <int D>
+__global__ __launch_bounds__(kCombineThreads) void attn_combine_kernel(AttnArgs a) {
+  constexpr int GL = D / 4;                  // threads per row
+  constexpr int RPB = kCombineThreads / GL;  // rows per block
+  __shared__ float wsh[RPB][kCombineMaxS];
+  const int u = blockIdx.y, tid = threadIdx.x;
+  const int r = tid / GL, g = tid % GL;
+  const int row = blockIdx.x * RPB + r;
+  const bool live = row < a.R;
+  const int S = a.S;
+  const size_t base = (size_t)u * S * a.R + row;   // partial index of split 0
+
+  // Row max over the splits (group of GL lanes, aligned within a wave).
+  float mx = kNegInf;
+  if (live)
+    for (int sp = g; sp < S; sp += GL) mx = fmaxf(mx, a.part_ml[(base + (size_t)sp * a.R) * 2]);
+#pragma unroll
+  for (int off = 1; off < GL; off <<= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+  // Split weights into LDS and the weighted sum of the row sums.
+  float den = 0.f;
+  if (live)
+    for (int sp = g; sp < S; sp += GL) {
+      const size_t pi = base + (size_t)sp * a.R;
+      const float ms = a.part_ml[pi * 2];
+      const float w = ms == kNegInf ? 0.f : fast_exp2(ms - mx);
+      wsh[r][sp] = w;
+      den = fmaf(w, a.part_ml[pi * 2 + 1], den);
+    }
+#pragma unroll
+  for (int off = 1; off < GL; off <<= 1) den += __shfl_xor(den, off);
+  __syncthreads();
+  if (!live) return;
+  f32x4_t num = {0.f, 0.f, 0.f, 0.f};
+  const float* po = a.part_o + base * D + 4 * g;
+  const size_t stride = (size_t)a.R * D;
+#pragma unroll 4
+  for (int sp = 0; sp < S; ++sp) num += wsh[r][sp] * *(const f32x4_t*)(po + sp * stride);
   const int b = u / a.Hkv, gk = u % a.Hkv;
   const int t = row / a.G, h = gk * a.G + row % a.G;
-  const size_t base = (size_t)u * a.S * a.R + row;
-  float mx = kNegInf;
-  for (int s = 0; s < a.S; ++s) mx = fmaxf(mx, a.part_ml[(base + (size_t)s * a.R) * 2]);
-  float num = 0.f, den = 0.f;
-  for (int s = 0; s < a.S; ++s) {
-    const size_t p = base + (size_t)s * a.R;
-    const float ms = a.part_ml[p * 2];
-    if (ms == kNegInf) continue;
-    const float w = fast_exp2(ms - mx);
-    den = fmaf(w, a.part_ml[p * 2 + 1], den);
-    num = fmaf(w, a.part_o[p * a.D + d], num);
-  }
-  a.out[(((size_t)b * a.T + t) * a.Hq + h) * a.D + d] = num / den;
+  *(f32x4_t*)(a.out + (((size_t)b * a.T + t) * a.Hq + h) * D + 4 * g) = num / den;
 }
 
 // ---------------------------------------------------------------------------
@@ -800,6 +829,7 @@ AttnPlan plan_attention(int B, int T, int Hq, int Hkv, int D, int ctx, int bf16)
   }
   const int min_chunk = SV_MIN_CHUNK;
   int S = (blocks_target + units * p.row_chunks - 1) / (units * p.row_chunks);
+  if (S > kCombineMaxS) S = kCombineMaxS;
   const int s_max = (L + min_chunk - 1) / min_chunk;
   if (S > s_max) S = s_max;
   if (S < 1) S = 1;
@@ -835,7 +865,10 @@ hipError_t launch_attention(const AttnPlan& p, const void* q, const void* k, con
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || (p.mfma && p.splits == 1)) return e;
-  attn_combine_kernel<<<dim3(p.rows, B * Hkv), D, 0, st>>>(a);
+  const int rpb = kCombineThreads / (D / 4);
+  const dim3 gc((p.rows + rpb - 1) / rpb, B * Hkv);
+  if (D == 64) attn_combine_kernel<64><<<gc, kCombineThreads, 0, st>>>(a);
+  else attn_combine_kernel<128><<<gc, kCombineThreads, 0, st>>>(a);
   return hipGetLastError();
 }
 

@@ -79,6 +79,9 @@ spec_status spec_verify_attention(const void* q, const void* k, const void* v,
   if (!isfinite(scale) || !(scale > 0.f)) return SPEC_ERR_SHAPE;
   if (B == 0 || T == 0) return SPEC_OK;
   if (!q || !k || !v || !out || !workspace) return SPEC_ERR_NULL;
+  // q, k, v and out are read and written 16 bytes per lane
+  if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)out) % 16 != 0)
+    return SPEC_ERR_UNSUPPORTED;
   const sv::AttnPlan p = sv::plan_attention(B, T, Hq, Hkv, D, ctx, dtype == SPEC_BF16);
   if (workspace_bytes < p.total_bytes) return SPEC_ERR_WORKSPACE;
   const hipError_t e = sv::launch_attention(p, q, k, v, parents, out, B, T, Hq, Hkv, D, ctx,
