@@ -81,6 +81,9 @@ def test_reduced_workloads_elementwise(name):
     # a single key tile per block, and a key range that fills the LDS ring exactly
     ("one_key_tile", dict(T=3, Hq=32, Hkv=8, D=128, ctx=5, dtype="bf16")),
     ("ring_of_tiles_exact", dict(B=64, T=8, ctx=248, dtype="bf16")),
+    # one KV head and a long prefix: more key splits than threads per row in the combine
+    ("many_splits_d128", dict(B=1, T=3, Hq=4, Hkv=1, D=128, ctx=20000, dtype="bf16")),
+    ("many_splits_d64", dict(B=1, T=2, Hq=8, Hkv=1, D=64, ctx=9000, dtype="bf16")),
     # two and three 16-row tiles per wave at D = 64
     ("d64_two_row_tiles", dict(T=32, Hq=64, Hkv=8, D=64, ctx=333, dtype="bf16")),
     ("d64_three_row_tiles", dict(T=40, Hq=64, Hkv=8, D=64, ctx=260, dtype="bf16")),

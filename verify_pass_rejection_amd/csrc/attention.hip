@@ -348,10 +348,10 @@ __device__ __forceinline__ float group4_sum(float x) {
 // Loading.  The block is W compute waves plus one loader wave.  The loader
 // streams the block's key range through a ring of P LDS slots of one 32-key
 // K/V tile each with direct-to-LDS loads (global_load_lds, 16 bytes per lane
-// written straight into LDS), keeping AHEAD = P - 1 tiles in flight without
-// holding them in registers.  It waits for its own loads (s_waitcnt vmcnt)
-// and joins the block barrier: after barrier j, tile j is complete in slot
-// j % P and the slot of tile j-1 is free for tile j + AHEAD.  The compute
+// written straight into LDS), keeping AHEAD tiles in flight without holding
+// them in registers.  It waits for its own loads (s_waitcnt vmcnt) and joins
+// the block barrier: after barrier j, tile j is complete in slot j % P and a
+// slot no wave reads any more is refilled with tile j + AHEAD.  The compute
 // waves issue no global loads inside the key loop.  The loads are written as
 // inline assembly so that the compiler does not order LDS reads after them.
 //
@@ -379,12 +379,23 @@ struct MfmaLayout {
 };
 
 // Ring depth: four slots (72 KB at D = 128) keep two blocks per CU resident
-// for one-row-tile kernels; five for the larger ones (one block per CU).  The
+// for one-row-tile kernels; five or six for the larger ones (one block per CU).  The
 // loader's outstanding loads, (AHEAD - 1) * NIT, must fit the 6-bit vmcnt.
+#ifndef SV_MFMA_LAG
+#define SV_MFMA_LAG 1
+#endif
 template <int D, int RT>
 struct MfmaRing {
-  static constexpr int P = RT == 1 ? 4 : 5;
-  static constexpr int AHEAD = P - 1;
+  // LAG: with two compute waves per SIMD (more than four compute waves), the
+  // upper waves run half a tile behind (see the key loop), which keeps the
+  // previous tile's slot in use until the next barrier.  Measured: medusa
+  // tree (three row tiles) 115-118 -> 111 us; eagle2 tree (two row tiles)
+  // 95-98 -> 104-106 us, so only three-row-tile kernels lag.
+  static constexpr bool LAG = RT == 3 && SV_MFMA_LAG;
+  static constexpr int P = RT == 1 ? 4 : LAG ? 6 : 5;
+  static constexpr int AHEAD_MAX = 63 / MfmaLayout<D>::NIT + 1;   // (AHEAD-1)*NIT < 64
+  static constexpr int AHEAD = (LAG ? P - 2 : P - 1) < AHEAD_MAX ? (LAG ? P - 2 : P - 1)
+                                                                 : AHEAD_MAX;
   static_assert((AHEAD - 1) * MfmaLayout<D>::NIT < 64, "vmcnt range");
 };
 
@@ -474,6 +485,8 @@ void attn_mfma_kernel(AttnArgs a) {
         lds_dma16(vg + off, slot + LY::KHALF + g * LY::GSV);
       }
     };
+    // After barrier j the slot refilled with tile j + AHEAD is that of tile
+    // j - 1 (j - 2 with LAG: lagging waves still read tile j - 1).
     const int pre = min(RG::AHEAD, ntiles);
     for (int t = 0; t < pre; ++t) issue(t);
     for (int j = 0; j < ntiles; ++j) {
@@ -661,9 +674,28 @@ void attn_mfma_kernel(AttnArgs a) {
     sexp(clean_tag, st, pf);
     pv(slot_of(it), pf);
   };
+  // Waves 0-3 and 4-7 share the four SIMDs (waves are placed round-robin).
+  // With LAG the upper waves apply P.V of the previous tile right after each
+  // barrier and the current tile's P.V after the next one: while a lower wave
+  // exponentiates, its partner computes scores, and the reverse.
+  auto step_lag = [&](auto clean_tag, int it, bf16x8_t (&pprev)[RT]) SV_INLINE {
+    ring_barrier();
+    if (it > 0) pv(slot_of(it - 1), pprev);
+    f32x4_t st[RT][2];
+    qk(slot_of(it), st);
+    smax(clean_tag, st, kb + it * KT);
+    sexp(clean_tag, st, pprev);
+  };
   int it = 0;
-  for (; it < ntiles && it < nclean; ++it) step(kClean, it);
-  for (; it < ntiles; ++it) step(kMasked, it);
+  if (RG::LAG && wave >= 4) {
+    bf16x8_t pprev[RT];
+    for (; it < ntiles && it < nclean; ++it) step_lag(kClean, it, pprev);
+    for (; it < ntiles; ++it) step_lag(kMasked, it, pprev);
+    pv(slot_of(ntiles - 1), pprev);              // the loader has stopped: slot intact
+  } else {
+    for (; it < ntiles && it < nclean; ++it) step(kClean, it);
+    for (; it < ntiles; ++it) step(kMasked, it);
+  }
 
   // Row sums over the four lane groups (every lane of a row gets the total).
   float lt[RT];
