@@ -24,6 +24,7 @@ Modules:
 * :mod:`oracle.attention` — masked verify attention by its plain definition.
 * :mod:`oracle.accept`    — chain rejection sampling and greedy tree acceptance.
 * :mod:`oracle.model`     — the α / expected-tokens / speedup closed forms.
+* :mod:`oracle.commit`    — the KV commit of the accepted path (a gather).
 
 Parity status: every function here is pinned by ``-m "not gpu"`` tests against
 something other than itself (a library routine, a closed form, brute force,
