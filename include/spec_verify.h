@@ -163,6 +163,39 @@ spec_status spec_accept_tree(const float* target_logits, const int32_t* tokens,
                              int B, int T, int V,
                              void* workspace, size_t workspace_bytes, void* hip_stream);
 
+/* ---------------------------------------------------------------------------
+ * KV commit after acceptance (Primer §9.1: at the first divergence the engine
+ * commits to the target's choice and drops the rest; glossary "Limites du
+ * parallel decoding": tree attention keeps every branch's keys and values in
+ * an enlarged cache, of which one branch survives verification).
+ *
+ * The verify pass found the T new positions' keys and values at rows
+ * ctx..ctx+T-1 (see spec_verify_attention).  For every sequence b and KV head
+ * g, with l = accept_len[b]:
+ *
+ *   K[b,g,ctx+i,:] <- K[b,g,ctx+path[b][i],:]   and the same for V, i = 0..l
+ *   new_len[b] = ctx + l + 1
+ *
+ * i.e. the cache becomes the prefix followed by the accepted path, root first
+ * (row ctx is the root, the last verified token).  Rows from new_len on are
+ * left as they are.  The token emitted after the path (the target's own
+ * choice, or the bonus token) has no key or value yet: the next pass computes
+ * them.  A chain (path == NULL) already has its accepted positions in place:
+ * only new_len is written, and k and v may then be NULL.
+ *
+ *   k, v        [B, Hkv, ctx+T, D]  dtype, modified in place; 16-byte aligned
+ *   path        [B, T] int32 or NULL: node ids root..l then -1, as returned by
+ *               spec_accept_tree (an entry outside [0, T) leaves row ctx+i as it is)
+ *   accept_len  [B] int32: spec_accept_tree's accept_len, or spec_accept_chain's
+ *               num_accepted (clamped to [0, T-1] on the device)
+ *   new_len     [B] int32 out
+ *
+ * Limits: 1 <= T <= 64, D in {64, 128}, Hkv >= 1, ctx >= 0.  No workspace.
+ * ------------------------------------------------------------------------- */
+spec_status spec_commit_kv(void* k, void* v, const int32_t* path, const int32_t* accept_len,
+                           int32_t* new_len, int B, int T, int Hkv, int D, int ctx,
+                           spec_dtype dtype, void* hip_stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -25,7 +25,7 @@ def declared_functions():
 def test_library_loads_and_exports_every_declared_symbol():
     lib = nat.load()
     decl = declared_functions()
-    assert len(decl) == 7
+    assert len(decl) == 8
     for name in decl:
         assert hasattr(lib, name), name
     assert sorted(nat.exported_symbols()) == decl
@@ -141,3 +141,25 @@ def test_python_binding_checks_tensors_before_calling():
     with pytest.raises(TypeError):
         nat.spec_accept_chain(torch.zeros(1, 2, 5), torch.zeros(1, 1, 5), torch.zeros(1, 1),
                               torch.zeros(1, 1), torch.zeros(1, 2))
+
+
+def commit(**kw):
+    a = dict(k=FAKE, v=FAKE, path=FAKE, acc=FAKE, new_len=FAKE, B=2, T=9, Hkv=8, D=128,
+             ctx=100, dtype=1, stream=None)
+    a.update(kw)
+    return nat.load().spec_commit_kv(a["k"], a["v"], a["path"], a["acc"], a["new_len"], a["B"],
+                                     a["T"], a["Hkv"], a["D"], a["ctx"], a["dtype"], a["stream"])
+
+
+def test_commit_validation():
+    assert commit(acc=None) == NULL
+    assert commit(new_len=None) == NULL
+    assert commit(k=None) == NULL              # a tree commit moves rows
+    assert commit(T=0) == SHAPE
+    assert commit(Hkv=0) == SHAPE
+    assert commit(ctx=-1) == SHAPE
+    assert commit(T=65) == UNSUP
+    assert commit(D=32) == UNSUP
+    assert commit(dtype=3) == UNSUP
+    assert commit(v=FAKE + 8) == UNSUP         # 16-byte vectors
+    assert commit(B=0, acc=None) == OK         # empty problem: nothing launched

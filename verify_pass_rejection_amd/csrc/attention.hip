@@ -562,7 +562,7 @@ void attn_mfma_kernel(AttnArgs a) {
   lds_u8* const ring3 = (lds_u8*)ring;
   // The slot offset goes through readfirstlane: an opaque wave-uniform value,
   // so that every fragment address is one base plus an immediate offset.
-  auto slot_of = [&](int t) -> lds_u8* SV_INLINE {
+  auto slot_of = [&](int t) SV_INLINE -> lds_u8* {
     return ring3 + __builtin_amdgcn_readfirstlane((t % P) * LY::SLOT);
   };
 

@@ -22,6 +22,9 @@ TreePlan plan_tree(int B, int T, int V);
 hipError_t launch_tree(const TreePlan& p, const float* logits, const int32_t* tokens,
                        const int32_t* parents, int32_t* accept_len, int32_t* path,
                        int32_t* out, int B, int T, int V, void* workspace, hipStream_t st);
+hipError_t launch_commit(void* k, void* v, const int32_t* path, const int32_t* accept_len,
+                         int32_t* new_len, int B, int T, int Hkv, int D, int ctx, int esize,
+                         hipStream_t st);
 }  // namespace sv
 
 namespace {
@@ -135,6 +138,24 @@ spec_status spec_accept_tree(const float* target_logits, const int32_t* tokens,
   const hipError_t e = sv::launch_tree(p, target_logits, tokens, parents, accept_len, path,
                                        out_tokens, B, T, V, workspace,
                                        (hipStream_t)hip_stream);
+  return e == hipSuccess ? SPEC_OK : SPEC_ERR_HIP;
+}
+
+spec_status spec_commit_kv(void* k, void* v, const int32_t* path, const int32_t* accept_len,
+                           int32_t* new_len, int B, int T, int Hkv, int D, int ctx,
+                           spec_dtype dtype, void* hip_stream) {
+  if (B < 0 || T < 1 || Hkv < 1 || D < 1 || ctx < 0) return SPEC_ERR_SHAPE;
+  if (dtype != SPEC_F32 && dtype != SPEC_BF16) return SPEC_ERR_UNSUPPORTED;
+  if (T > SPEC_MAX_T || (D != 64 && D != 128)) return SPEC_ERR_UNSUPPORTED;
+  if ((long long)(ctx + T) * D >= (1ll << 31)) return SPEC_ERR_UNSUPPORTED;
+  if (B == 0) return SPEC_OK;
+  if (!accept_len || !new_len) return SPEC_ERR_NULL;
+  if (path != nullptr) {
+    if (!k || !v) return SPEC_ERR_NULL;
+    if (((uintptr_t)k | (uintptr_t)v) % 16 != 0) return SPEC_ERR_UNSUPPORTED;
+  }
+  const hipError_t e = sv::launch_commit(k, v, path, accept_len, new_len, B, T, Hkv, D, ctx,
+                                         dtype == SPEC_BF16 ? 2 : 4, (hipStream_t)hip_stream);
   return e == hipSuccess ? SPEC_OK : SPEC_ERR_HIP;
 }
 

@@ -32,6 +32,7 @@ _SIGNATURES = {
     "spec_accept_tree_workspace": (_c.c_size_t, [_c.c_int] * 3),
     "spec_accept_tree": (_c.c_int, [_c.c_void_p] * 6 + [_c.c_int] * 3
                          + [_c.c_void_p, _c.c_size_t, _c.c_void_p]),
+    "spec_commit_kv": (_c.c_int, [_c.c_void_p] * 5 + [_c.c_int] * 5 + [_c.c_int, _c.c_void_p]),
 }
 
 _lib = None
@@ -199,3 +200,22 @@ def spec_accept_tree(target_logits, tokens, parents, accept_len=None, path=None,
                                  _ptr(ws), ws.numel() * ws.element_size(), _stream(stream))
     _raise(st, "spec_accept_tree")
     return accept_len, path, out_tokens
+
+
+def spec_commit_kv(k, v, ctx, accept_len, path=None, new_len=None, stream=None):
+    """Commit the accepted path's K/V in place; returns new_len [B] (int32)."""
+    B, Hkv, L, D = k.shape
+    T = L - ctx
+    dev = k.device
+    dt = {torch.float32: SPEC_F32, torch.bfloat16: SPEC_BF16}[k.dtype]
+    _check(k, "k", (B, Hkv, L, D), k.dtype, dev)
+    _check(v, "v", (B, Hkv, L, D), k.dtype, dev)
+    _check(accept_len, "accept_len", (B,), torch.int32, dev)
+    if path is not None:
+        _check(path, "path", (B, T), torch.int32, dev)
+    if new_len is None:
+        new_len = torch.empty(B, dtype=torch.int32, device=dev)
+    st = load().spec_commit_kv(_ptr(k), _ptr(v), _ptr(path), _ptr(accept_len), _ptr(new_len),
+                               B, T, Hkv, D, ctx, dt, _stream(stream))
+    _raise(st, "spec_commit_kv")
+    return new_len
