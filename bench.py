@@ -263,7 +263,7 @@ def main():
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
-              "(the verify step shards with no exchange over batch or KV heads; see DESIGN.md)",
+              "(the verify step shards with no exchange over batch or KV heads)",
               file=sys.stderr)
         sys.exit(2)
 

@@ -25,6 +25,8 @@ Modules:
 * :mod:`oracle.accept`    — chain rejection sampling and greedy tree acceptance.
 * :mod:`oracle.model`     — the α / expected-tokens / speedup closed forms.
 * :mod:`oracle.commit`    — the KV commit of the accepted path (a gather).
+* :mod:`oracle.paged`     — verify attention over a paged KV cache (a gather
+  of each sequence's pages, then :mod:`oracle.attention`).
 
 Parity status: every function here is pinned by ``-m "not gpu"`` tests against
 something other than itself (a library routine, a closed form, brute force,

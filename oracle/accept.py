@@ -22,7 +22,7 @@ engine commits to the target's own choice at the first divergence.  The check
 is greedy (the mc2informatique article, step 2: do the drafts match the target's
 own predictions).
 
-Readings where the pages are silent (also listed in the design doc):
+Readings where the pages are silent:
 
 * the ratio test is ``u < r`` with caller uniforms u in (0, 1); one u_accept per
   draft position and one u_draw per position, only the draw at the stopping

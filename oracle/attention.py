@@ -16,7 +16,7 @@ conditions on.  For a linear chain those are the earlier draft positions
 Primer §9.2 on EAGLE-2) a node conditions on its ancestors only, and the
 attention mask encodes the tree.
 
-Readings where the pages are silent (listed again in the design doc):
+Readings where the pages are silent:
 
 * scale defaults to 1/sqrt(D) (scaled dot-product attention);
 * Q and K arrive already position-encoded: no rotary step here;

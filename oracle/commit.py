@@ -16,7 +16,7 @@ positions only, and the rest is dropped:
   LLM" (mc2informatique.fr), section "Comment fonctionne le décodage
   spéculatif ?", step 3: the validated tokens are kept.
 
-Reading where the pages are silent (also listed in the design doc): position 0 of
+Reading where the pages are silent: position 0 of
 the new rows is the root (the last verified token) and is always kept; the
 accepted path root = path[0], ..., path[l] (l = accept_len) is moved to rows
 ctx .. ctx+l in path order and the cache length becomes ctx + l + 1; rows past

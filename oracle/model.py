@@ -10,7 +10,7 @@ per-token acceptance 0.8 and near 10–12 at 0.9, and as acceptance tends to 1 t
 speedup tends to 1/α.  §9.1 adds that a verify pass at N = 4 costs about
 1.2–1.5 decode steps.
 
-Readings (also in the design doc): the expected token count includes the bonus
+Readings: the expected token count includes the bonus
 token drawn from p_N, so with a constant per-token acceptance a it is
 1 + a + … + a^N; the draft time is the whole round's drafting time; α is
 measured as (T_verify(N) − T_verify(0)) / (N · T_verify(0)).

@@ -27,7 +27,7 @@ import torch
 # Named substreams: a per-input offset added to the workload seed.
 _STREAMS = {"q": 1, "k": 2, "v": 3, "target": 4, "draft_noise": 5,
             "draft_gumbel": 6, "u_accept": 7, "u_draw": 8, "tree": 9,
-            "tree_tokens": 10}
+            "tree_tokens": 10, "ctx_lens": 11, "pages": 12}
 
 #: Spike written into a parent's logit row at the planted child's token, in
 #: units of the logit standard deviation (8σ is never reached by N(0, σ²)
@@ -239,6 +239,67 @@ def make_tree_inputs(w: Workload, device="cpu"):
                     tokens[b, c] = int(torch.randint(0, V, (1,), generator=gk))
     return dict(target_logits=logits, tokens=tokens.to(torch.int32).to(device),
                 parents=parents.to(device))
+
+
+def ragged_ctx_lens(w: Workload, device="cpu") -> torch.Tensor:
+    """Per-sequence prefix lengths [B] int32 for a paged cache: uniform in
+    [0, ctx], with sequence 0 at ctx (the longest) and, for B >= 3, the last
+    sequence at 0 (no prefix)."""
+    g = _gen(w, "ctx_lens", "cpu")
+    lens = torch.randint(0, w.ctx + 1, (w.B,), generator=g, dtype=torch.int64)
+    lens[0] = w.ctx
+    if w.B >= 3:
+        lens[-1] = 0
+    return lens.to(torch.int32).to(device)
+
+
+def make_paged_kv(w: Workload, k: torch.Tensor, v: torch.Tensor, page_size: int,
+                  layout: str = "hnd", ctx_lens=None, spare_pages: int = 3):
+    """Scatter contiguous K/V [B, Hkv, ctx+T, D] into a shuffled page pool.
+
+    Sequence b keeps its first ctx_lens[b] + T rows (all ctx + T rows when
+    ctx_lens is None).  Its j-th block of page_size rows goes to the page that
+    a seeded permutation of the pool assigns it; block_table[b][j] names that
+    page.  The pool holds spare_pages pages more than the sequences use.
+    Everything no sequence owns is NaN: rows past a sequence's length in its
+    last page, the spare pages, and the page that the unused block-table
+    entries (past each sequence's last block) point at.
+
+    Returns (k_pages, v_pages, block_table [B, max_blocks] int32) on k's
+    device; pages are [P, Hkv, page_size, D] ("hnd") or [P, page_size, Hkv,
+    D] ("nhd").
+    """
+    B, Hkv, L, D = k.shape
+    T = w.T
+    lens = [L - T] * B if ctx_lens is None else [int(x) for x in ctx_lens]
+    nblk = [(c + T + page_size - 1) // page_size for c in lens]
+    max_blocks = (L + page_size - 1) // page_size
+    used = sum(nblk)
+    pool = used + max(1, spare_pages)
+    perm = torch.randperm(pool, generator=_gen(w, "pages", "cpu"))
+    poison = int(perm[used])                      # a spare page: stale entries point here
+    table = torch.full((B, max_blocks), poison, dtype=torch.int32)
+    shape = (pool, Hkv, page_size, D) if layout == "hnd" else (pool, page_size, Hkv, D)
+    if layout not in ("hnd", "nhd"):
+        raise ValueError(f"unknown page layout {layout!r}")
+    pages = []
+    for src in (k, v):
+        dst = torch.full(shape, float("nan"), dtype=src.dtype, device=src.device)
+        at = 0
+        for b in range(B):
+            n, rows = nblk[b], lens[b] + T
+            ids = perm[at: at + n]
+            at += n
+            table[b, :n] = ids.to(torch.int32)
+            blk = torch.full((Hkv, n * page_size, D), float("nan"), dtype=src.dtype,
+                             device=src.device)
+            blk[:, :rows] = src[b, :, :rows]
+            blk = blk.view(Hkv, n, page_size, D).permute(1, 0, 2, 3)   # [n, Hkv, ps, D]
+            if layout == "nhd":
+                blk = blk.permute(0, 2, 1, 3)                          # [n, ps, Hkv, D]
+            dst[ids.to(src.device)] = blk
+        pages.append(dst)
+    return pages[0], pages[1], table.to(k.device)
 
 
 def default_scale(D: int) -> float:
