@@ -104,6 +104,59 @@ spec_status spec_verify_attention(const void* q, const void* k, const void* v,
                                   void* hip_stream);
 
 /* ---------------------------------------------------------------------------
+ * Verify attention over a paged KV cache.
+ *
+ * Serving engines keep the cache in pages ("LLM Primer VI", closing section
+ * "Ce que prépare le Chapitre 9": paged KV is one of the runtime tools an
+ * engine wires together with speculative decoding; "Parallel Decoding"
+ * glossary, "Parallel decoding en production": the engines that run
+ * speculation).  The operation is spec_verify_attention's, for every sequence
+ * b with a prefix length of its own, ctx_b, and its keys and values in pages
+ * of a shared pool: position i (0 <= i < ctx_b + T) of sequence b is row
+ * i % page_size of page block_table[b][i / page_size]; positions ctx_b ..
+ * ctx_b + T - 1 hold the T new positions.
+ *
+ *   q            [B, T, Hq, D]                 dtype
+ *   k_pages,     SPEC_PAGES_HND: [num_pages, Hkv, page_size, D]
+ *   v_pages      SPEC_PAGES_NHD: [num_pages, page_size, Hkv, D]   dtype
+ *   block_table  [B, max_blocks] int32 page ids; entries past a sequence's
+ *                last page are never read
+ *   ctx_lens     [B] int32 prefix lengths, each in [0, max_ctx]; NULL: all max_ctx
+ *   parents      [B, T] int32 or NULL, as for spec_verify_attention
+ *   out          [B, T, Hq, D] float32
+ *   max_ctx      the largest prefix length; sizes the launch and the workspace
+ *                (spec_verify_attention_paged_workspace)
+ *
+ * Rows of a page past its sequence's length, and pages no table entry in
+ * use names, are never read.  Not checked on the device (memory-safe, results
+ * unspecified): ctx_lens outside [0, max_ctx] are clamped into it, page ids
+ * outside [0, num_pages) are clamped into the pool.
+ * Limits: those of spec_verify_attention, and page_size a power of two no
+ * larger than SPEC_MAX_PAGE_SIZE, num_pages >= 1, max_blocks * page_size >=
+ * max_ctx + T; q, k_pages, v_pages and out 16-byte aligned.  With equal
+ * prefix lengths the result is bit-identical to spec_verify_attention's on
+ * the same logical cache.
+ * ------------------------------------------------------------------------- */
+typedef enum {
+    SPEC_PAGES_HND = 0,        /* a page holds each KV head's rows contiguously   */
+    SPEC_PAGES_NHD = 1         /* a page holds each position's KV heads together  */
+} spec_page_layout;
+
+#define SPEC_MAX_PAGE_SIZE (1 << 20)
+
+size_t spec_verify_attention_paged_workspace(int B, int T, int Hq, int Hkv, int D, int max_ctx,
+                                             spec_dtype dtype);
+
+spec_status spec_verify_attention_paged(const void* q, const void* k_pages, const void* v_pages,
+                                        const int32_t* block_table, const int32_t* ctx_lens,
+                                        const int32_t* parents, float* out,
+                                        int B, int T, int Hq, int Hkv, int D, int max_ctx,
+                                        int page_size, int num_pages, int max_blocks,
+                                        spec_page_layout layout, spec_dtype dtype, float scale,
+                                        void* workspace, size_t workspace_bytes,
+                                        void* hip_stream);
+
+/* ---------------------------------------------------------------------------
  * Chain acceptance by rejection sampling (Primer §9.1).
  *
  * With p_i = softmax(target_logits[b,i,:] / temperature) (i = 0..N) and

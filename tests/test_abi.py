@@ -25,7 +25,7 @@ def declared_functions():
 def test_library_loads_and_exports_every_declared_symbol():
     lib = nat.load()
     decl = declared_functions()
-    assert len(decl) == 8
+    assert len(decl) == 10
     for name in decl:
         assert hasattr(lib, name), name
     assert sorted(nat.exported_symbols()) == decl
@@ -80,6 +80,42 @@ def test_attention_workspace_sizes():
     assert f(0, 5, 8, 8, 64, 256, nat.SPEC_F32) == 0
     # the workspace holds at least one partial (D floats + max and sum) per row and split
     assert f(2, 6, 32, 8, 128, 4096, nat.SPEC_BF16) >= 2 * 8 * 24 * 130 * 4
+
+
+def paged(**kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, bt=FAKE, lens=FAKE, parents=None, out=FAKE, B=2, T=5, Hq=8,
+             Hkv=2, D=128, max_ctx=100, ps=16, P=20, mb=7, layout=0, dtype=1, scale=0.1,
+             ws=FAKE, ws_bytes=1 << 40, stream=None)
+    a.update(kw)
+    return nat.load().spec_verify_attention_paged(
+        a["q"], a["k"], a["v"], a["bt"], a["lens"], a["parents"], a["out"], a["B"], a["T"],
+        a["Hq"], a["Hkv"], a["D"], a["max_ctx"], a["ps"], a["P"], a["mb"], a["layout"],
+        a["dtype"], a["scale"], a["ws"], a["ws_bytes"], a["stream"])
+
+
+def test_paged_attention_validation():
+    assert paged(q=None) == NULL
+    assert paged(k=None) == NULL
+    assert paged(bt=None) == NULL
+    assert paged(ws=None) == NULL
+    assert paged(Hq=7) == SHAPE
+    assert paged(max_ctx=-1) == SHAPE
+    assert paged(ps=0) == SHAPE
+    assert paged(P=0) == SHAPE
+    assert paged(mb=6) == SHAPE               # 6 * 16 < 100 + 5: the table is too short
+    assert paged(ps=24) == UNSUP              # page sizes are powers of two
+    assert paged(ps=1 << 21) == UNSUP
+    assert paged(layout=2) == UNSUP
+    assert paged(T=65) == UNSUP
+    assert paged(D=96) == UNSUP
+    assert paged(scale=0.0) == SHAPE
+    assert paged(ws_bytes=16) == WS
+    assert paged(k=FAKE + 2) == UNSUP         # 16-byte loads need alignment
+    assert paged(B=0, q=None) == OK
+    assert paged(T=0, q=None) == OK
+    f = nat.spec_verify_attention_paged_workspace
+    assert f(64, 9, 32, 8, 128, 32768, nat.SPEC_BF16) == \
+        nat.spec_verify_attention_workspace(64, 9, 32, 8, 128, 32768, nat.SPEC_BF16)
 
 
 def chain(**kw):

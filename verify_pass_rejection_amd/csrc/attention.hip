@@ -42,15 +42,40 @@ typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
 struct AttnArgs {
   const void* q;           // [B, T, Hq, D]
-  const void* k;           // [B, Hkv, L, D]
-  const void* v;           // [B, Hkv, L, D]
+  const void* k;           // [B, Hkv, L, D], or the page pool of a paged cache
+  const void* v;           // [B, Hkv, L, D], or the page pool of a paged cache
   const int32_t* parents;  // [B, T] or nullptr (chain)
   float* out;              // [B, T, Hq, D]
   float* part_o;           // [units, S, R, D]  unnormalised partial outputs
   float* part_ml;          // [units, S, R, 2]  (running max in log2 units, sum)
   int B, T, Hq, Hkv, G, D, ctx, L, R, S, chunk;
   float scale_log2;        // softmax scale * log2(e)
+  // Paged cache (the PAGED kernels only): position i of sequence b is row
+  // i % page_size of page block_table[b][i / page_size]; ctx is then the
+  // largest prefix and L = ctx + T the largest sequence.
+  const int32_t* block_table;    // [B, max_blocks]
+  const int32_t* ctx_lens;       // [B] prefix lengths, or nullptr (all ctx)
+  int page_shift, max_blocks, num_pages;
+  int64_t page_stride, head_stride, row_stride;   // elements
 };
+
+// Prefix length of sequence b: its own in a paged cache (clamped to
+// [0, ctx], so a bad length cannot reach past the planned key range).
+template <bool PAGED>
+__device__ __forceinline__ int seq_ctx(const AttnArgs& a, int b) {
+  if constexpr (PAGED) {
+    if (a.ctx_lens != nullptr) return min(max(a.ctx_lens[b], 0), a.ctx);
+  }
+  return a.ctx;
+}
+
+// Element offset of row `key` of KV head g in page `page` of the pool (page
+// ids outside the pool are clamped into it: wrong but in-bounds data).
+__device__ __forceinline__ size_t paged_row(const AttnArgs& a, int page, int g, int key) {
+  page = min(max(page, 0), a.num_pages - 1);
+  return (size_t)page * a.page_stride + (size_t)g * a.head_stride +
+         (size_t)(key & ((1 << a.page_shift) - 1)) * a.row_stride;
+}
 
 // Ancestor-or-self masks of the T query positions of sequence b, into LDS.
 // Each position walks up its parents (a chain needs no walk).  A parent that
@@ -139,7 +164,7 @@ __device__ __forceinline__ float group_sum(float v) {
   return v;
 }
 
-template <int D, int RMAX>
+template <int D, int RMAX, bool PAGED>
 __global__ __launch_bounds__(256)
 __attribute__((amdgpu_waves_per_eu(RMAX <= 4 ? SV_VALU_WAVES_PER_EU : 1)))
 void attn_valu_kernel(AttnArgs a) {
@@ -185,11 +210,13 @@ void attn_valu_kernel(AttnArgs a) {
   for (int r = 0; r < RMAX; ++r) settle(qw[r]);
 #endif
 
-  // This block's keys, cut into 4 contiguous per-wave ranges.
-  const int kb = s * a.chunk, ke = min(a.L, kb + a.chunk);
+  // This block's keys, cut into 4 contiguous per-wave ranges (a split past
+  // the end of a shorter paged sequence has none).
+  const int ctx = seq_ctx<PAGED>(a, b), L = ctx + a.T;
+  const int kb = s * a.chunk, ke = max(kb, min(L, kb + a.chunk));
   const int per = ((ke - kb + 3) / 4 + KPI - 1) / KPI * KPI;
   const int wb = kb + wave * per, we = min(ke, wb + per);
-  const int clean_end = min(a.ctx, we);
+  const int clean_end = min(ctx, we);
   const float c = a.scale_log2;
 
   float m[RMAX], l[RMAX], o[RMAX][EPL];
@@ -201,16 +228,20 @@ void attn_valu_kernel(AttnArgs a) {
     for (int e = 0; e < EPL; ++e) o[r][e] = 0.f;
   }
 
-  const size_t unit_off = (size_t)u * a.L * D;
+  const size_t unit_off = PAGED ? 0 : (size_t)u * a.L * D;
   const float* kp = (const float*)a.k + unit_off + dp * EPL;
   const float* vp = (const float*)a.v + unit_off + dp * EPL;
-  const int last = a.L - 1;
+  const int32_t* bt = a.block_table + (PAGED ? (size_t)b * a.max_blocks : 0);
+  const int last = L - 1;
 
   u32x4_t kw[U], vw[U];
   auto load = [&](int key0) {
 #pragma unroll
     for (int j = 0; j < U; ++j) {
-      const uint32_t off = (uint32_t)(min(key0 + j * KPS + ks, last) * D);
+      const int key = min(key0 + j * KPS + ks, last);
+      size_t off;
+      if constexpr (PAGED) off = paged_row(a, bt[key >> a.page_shift], g, key);
+      else off = (uint32_t)(key * D);
       kw[j] = *(const u32x4_t*)(kp + off);
       vw[j] = *(const u32x4_t*)(vp + off);
     }
@@ -241,7 +272,7 @@ void attn_valu_kernel(AttnArgs a) {
         sc[j] = group_sum<LPK>(acc);
         if (!clean) {
           const int key = key0 + j * KPS + ks;
-          if (!(key < we && tail_visible(mrow[r], key, a.ctx))) sc[j] = kNegInf;
+          if (!(key < we && tail_visible(mrow[r], key, ctx))) sc[j] = kNegInf;
         }
       }
       float mt = sc[0];
@@ -413,6 +444,10 @@ __device__ __forceinline__ void lds_dma16(const void* g, uint32_t lds) {
   asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "{m0}"(lds) : "memory");
 #endif
 }
+// The same with 4 bytes per lane (lane L writes lds + 4L): page ids.
+__device__ __forceinline__ void lds_dma4(const void* g, uint32_t lds) {
+  asm volatile("s_nop 0\n\tglobal_load_lds_dword %0, off" ::"v"(g), "{m0}"(lds) : "memory");
+}
 template <int N>
 __device__ __forceinline__ void wait_vm() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
@@ -434,7 +469,7 @@ __device__ __forceinline__ void ring_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
-template <int D, int RT, int W>
+template <int D, int RT, int W, bool PAGED>
 __global__ __launch_bounds__(64 * (W + 1))
 void attn_mfma_kernel(AttnArgs a) {
   using LY = MfmaLayout<D>;
@@ -447,6 +482,7 @@ void attn_mfma_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(1024))) uint8_t ring[P * LY::SLOT];
   __shared__ int par[64];
   __shared__ uint64_t masks[64];
+  __shared__ int ptab[PAGED ? P * 64 : 1];    // paged: page ids of the tiles in flight
 
   const int s = blockIdx.x, u = blockIdx.y, rc = blockIdx.z;
   const int b = u / a.Hkv, gk = u % a.Hkv;
@@ -456,9 +492,11 @@ void attn_mfma_kernel(AttnArgs a) {
 
   build_masks(a, b, par, masks);
 
-  const int kb = s * a.chunk, ke = min(a.L, kb + a.chunk);
+  // a split past the end of a shorter paged sequence has no tiles
+  const int ctx = seq_ctx<PAGED>(a, b), L = ctx + a.T;
+  const int kb = s * a.chunk, ke = max(kb, min(L, kb + a.chunk));
   const int ntiles = (ke - kb + KT - 1) / KT;
-  const size_t unit_off = (size_t)u * a.L * D;
+  const size_t unit_off = PAGED ? 0 : (size_t)u * L * D;
   const uint16_t* kg = (const uint16_t*)a.k + unit_off;
   const uint16_t* vg = (const uint16_t*)a.v + unit_off;
 
@@ -473,26 +511,81 @@ void attn_mfma_kernel(AttnArgs a) {
     }
     const uint32_t ring_lds =
         (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)ring;
+    // Paged: the ids of the (up to 32) pages under tile t are loaded, 64 at a
+    // time, into ptab[t % P] by the issue of tile t - AHEAD, as one more load
+    // of that issue, so the in-order wait for a tile also covers them.  Every
+    // issue loads them (clamped ids past the end) to keep NIT + 1 loads per tile.
+    const int32_t* bt = a.block_table + (PAGED ? (size_t)b * a.max_blocks : 0);
+    const int last_blk = PAGED ? (L - 1) >> a.page_shift : 0;
+    const uint32_t ptab_lds =
+        (uint32_t)(uintptr_t)(__attribute__((address_space(3))) int*)ptab;
+    auto fetch_pages = [&](int t) SV_INLINE {
+      const int idx = min(((kb + t * KT) >> a.page_shift) + lane, last_blk);
+      lds_dma4(bt + idx, ptab_lds + (uint32_t)((t % P) * 256));
+    };
     auto issue = [&](int t) SV_INLINE {
       const int key0 = kb + t * KT + lj;
       const uint32_t slot = ring_lds + (uint32_t)((t % P) * LY::SLOT);
 #pragma unroll
       for (int g = 0; g < LY::NG; ++g) {
         // keys past the end re-read the last row (finite data, masked later)
-        const int key = min(key0 + g * LY::KG, a.L - 1);
+        const int key = min(key0 + g * LY::KG, L - 1);
         const uint32_t off = (uint32_t)key * D + 8 * lc;
         lds_dma16(kg + off, slot + g * LY::GSK);
         lds_dma16(vg + off, slot + LY::KHALF + g * LY::GSV);
       }
     };
+    // Paged: every offset of a tile is computed (page ids read from LDS) before
+    // its first load is issued, so that the reads share one wait.
+    auto paged_offsets = [&](int t, size_t (&off)[LY::NG]) SV_INLINE {
+      const int key0 = kb + t * KT + lj;
+      const int first = (kb + t * KT) >> a.page_shift;
+#pragma unroll
+      for (int g = 0; g < LY::NG; ++g) {
+        const int key = min(key0 + g * LY::KG, L - 1);
+        off[g] = paged_row(a, ptab[(t % P) * 64 + (key >> a.page_shift) - first], gk, key) +
+                 8 * lc;
+      }
+    };
+    auto paged_issue = [&](int t, const size_t (&off)[LY::NG]) SV_INLINE {
+      const uint32_t slot = ring_lds + (uint32_t)((t % P) * LY::SLOT);
+#pragma unroll
+      for (int g = 0; g < LY::NG; ++g) {
+        lds_dma16(kg + off[g], slot + g * LY::GSK);
+        lds_dma16(vg + off[g], slot + LY::KHALF + g * LY::GSV);
+      }
+      fetch_pages(t + RG::AHEAD);
+    };
     // After barrier j the slot refilled with tile j + AHEAD is that of tile
     // j - 1 (j - 2 with LAG: lagging waves still read tile j - 1).
     const int pre = min(RG::AHEAD, ntiles);
-    for (int t = 0; t < pre; ++t) issue(t);
-    for (int j = 0; j < ntiles; ++j) {
-      wait_tiles<LY::NIT, RG::AHEAD - 1>(min(ntiles - 1 - j, RG::AHEAD - 1));
-      ring_barrier();
-      if (j + RG::AHEAD < ntiles) issue(j + RG::AHEAD);
+    if constexpr (PAGED) {
+      constexpr int C = LY::NIT + 1;                  // loads per issue
+      static_assert((RG::AHEAD - 1) * C < 64, "vmcnt range");
+      for (int t = 0; t < pre; ++t) fetch_pages(t);
+      wait_vm<0>();
+      for (int t = 0; t < pre; ++t) {
+        size_t off[LY::NG];
+        paged_offsets(t, off);
+        paged_issue(t, off);
+      }
+      for (int j = 0; j < ntiles; ++j) {
+        wait_tiles<C, RG::AHEAD - 1>(min(ntiles - 1 - j, RG::AHEAD - 1));
+        // the page ids of tile j + AHEAD came with tile j: read them while
+        // the compute waves reach the barrier
+        const bool more = j + RG::AHEAD < ntiles;
+        size_t off[LY::NG];
+        if (more) paged_offsets(j + RG::AHEAD, off);
+        ring_barrier();
+        if (more) paged_issue(j + RG::AHEAD, off);
+      }
+    } else {
+      for (int t = 0; t < pre; ++t) issue(t);
+      for (int j = 0; j < ntiles; ++j) {
+        wait_tiles<LY::NIT, RG::AHEAD - 1>(min(ntiles - 1 - j, RG::AHEAD - 1));
+        ring_barrier();
+        if (j + RG::AHEAD < ntiles) issue(j + RG::AHEAD);
+      }
     }
     return;
   }
@@ -556,7 +649,7 @@ void attn_mfma_kernel(AttnArgs a) {
 
   const float c = a.scale_log2;
   // tiles [0, nclean) lie wholly inside the prefix: every key visible, no mask
-  const int clean_end = min(a.ctx, ke);
+  const int clean_end = min(ctx, ke);
   const int nclean = clean_end > kb ? (clean_end - kb) / KT : 0;
   typedef __attribute__((address_space(3))) const uint8_t lds_u8;
   lds_u8* const ring3 = (lds_u8*)ring;
@@ -600,7 +693,7 @@ void attn_mfma_kernel(AttnArgs a) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const int key = base + (e < 4 ? 4 * g4 + e : 16 + 4 * g4 + e - 4);
-          if (!(key < ke && tail_visible(mrow[rt], key, a.ctx))) st[rt][e >> 2][e & 3] = kNegInf;
+          if (!(key < ke && tail_visible(mrow[rt], key, ctx))) st[rt][e >> 2][e & 3] = kNegInf;
         }
       }
       const f32x4_t x0 = st[rt][0], x1 = st[rt][1];
@@ -691,7 +784,7 @@ void attn_mfma_kernel(AttnArgs a) {
     bf16x8_t pprev[RT];
     for (; it < ntiles && it < nclean; ++it) step_lag(kClean, it, pprev);
     for (; it < ntiles; ++it) step_lag(kMasked, it, pprev);
-    pv(slot_of(ntiles - 1), pprev);              // the loader has stopped: slot intact
+    if (ntiles > 0) pv(slot_of(ntiles - 1), pprev);   // the loader has stopped: slot intact
   } else {
     for (; it < ntiles && it < nclean; ++it) step(kClean, it);
     for (; it < ntiles; ++it) step(kMasked, it);
@@ -778,40 +871,51 @@ __global__ __launch_bounds__(kCombineThreads) void attn_combine_kernel(AttnArgs 
 // ---------------------------------------------------------------------------
 // Host-side dispatch.
 // ---------------------------------------------------------------------------
-template <int D, int RT>
+template <int D, int RT, bool PG>
 static void launch_mfma_w(const AttnPlan& p, const AttnArgs& a, hipStream_t st, dim3 grid) {
   switch (p.waves) {
     // W compute waves + the loader wave
-    case 1: attn_mfma_kernel<D, RT, 1><<<grid, 128, 0, st>>>(a); break;
-    case 2: attn_mfma_kernel<D, RT, 2><<<grid, 192, 0, st>>>(a); break;
-    case 3: attn_mfma_kernel<D, RT, 3><<<grid, 256, 0, st>>>(a); break;
-    case 4: attn_mfma_kernel<D, RT, 4><<<grid, 320, 0, st>>>(a); break;
-    case 5: attn_mfma_kernel<D, RT, 5><<<grid, 384, 0, st>>>(a); break;
-    case 6: attn_mfma_kernel<D, RT, 6><<<grid, 448, 0, st>>>(a); break;
-    case 7: attn_mfma_kernel<D, RT, 7><<<grid, 512, 0, st>>>(a); break;
+    case 1: attn_mfma_kernel<D, RT, 1, PG><<<grid, 128, 0, st>>>(a); break;
+    case 2: attn_mfma_kernel<D, RT, 2, PG><<<grid, 192, 0, st>>>(a); break;
+    case 3: attn_mfma_kernel<D, RT, 3, PG><<<grid, 256, 0, st>>>(a); break;
+    case 4: attn_mfma_kernel<D, RT, 4, PG><<<grid, 320, 0, st>>>(a); break;
+    case 5: attn_mfma_kernel<D, RT, 5, PG><<<grid, 384, 0, st>>>(a); break;
+    case 6: attn_mfma_kernel<D, RT, 6, PG><<<grid, 448, 0, st>>>(a); break;
+    case 7: attn_mfma_kernel<D, RT, 7, PG><<<grid, 512, 0, st>>>(a); break;
     default:
       // three row tiles need more than the 168 registers that 9 waves per CU allow
-      if constexpr (RT < 3) attn_mfma_kernel<D, RT, 8><<<grid, 576, 0, st>>>(a);
+      if constexpr (RT < 3) attn_mfma_kernel<D, RT, 8, PG><<<grid, 576, 0, st>>>(a);
       break;
   }
 }
 
-template <int D>
+template <int D, bool PG>
 static void launch_mfma(const AttnPlan& p, const AttnArgs& a, hipStream_t st, dim3 grid) {
   switch (p.rt) {
-    case 1: launch_mfma_w<D, 1>(p, a, st, grid); break;
-    case 2: launch_mfma_w<D, 2>(p, a, st, grid); break;
-    default: launch_mfma_w<D, 3>(p, a, st, grid); break;
+    case 1: launch_mfma_w<D, 1, PG>(p, a, st, grid); break;
+    case 2: launch_mfma_w<D, 2, PG>(p, a, st, grid); break;
+    default: launch_mfma_w<D, 3, PG>(p, a, st, grid); break;
   }
 }
 
-template <int D>
+template <int D, bool PG>
 static void launch_valu(const AttnPlan& p, const AttnArgs& a, hipStream_t st, dim3 grid) {
   switch (p.rmax) {
-    case 1: attn_valu_kernel<D, 1><<<grid, 256, 0, st>>>(a); break;
-    case 2: attn_valu_kernel<D, 2><<<grid, 256, 0, st>>>(a); break;
-    case 4: attn_valu_kernel<D, 4><<<grid, 256, 0, st>>>(a); break;
-    default: attn_valu_kernel<D, 8><<<grid, 256, 0, st>>>(a); break;
+    case 1: attn_valu_kernel<D, 1, PG><<<grid, 256, 0, st>>>(a); break;
+    case 2: attn_valu_kernel<D, 2, PG><<<grid, 256, 0, st>>>(a); break;
+    case 4: attn_valu_kernel<D, 4, PG><<<grid, 256, 0, st>>>(a); break;
+    default: attn_valu_kernel<D, 8, PG><<<grid, 256, 0, st>>>(a); break;
+  }
+}
+
+template <bool PG>
+static void launch_main(const AttnPlan& p, const AttnArgs& a, hipStream_t st, dim3 grid) {
+  if (p.mfma) {
+    if (a.D == 64) launch_mfma<64, PG>(p, a, st, grid);
+    else launch_mfma<128, PG>(p, a, st, grid);
+  } else {
+    if (a.D == 64) launch_valu<64, PG>(p, a, st, grid);
+    else launch_valu<128, PG>(p, a, st, grid);
   }
 }
 
@@ -879,21 +983,32 @@ AttnPlan plan_attention(int B, int T, int Hq, int Hkv, int D, int ctx, int bf16)
 hipError_t launch_attention(const AttnPlan& p, const void* q, const void* k, const void* v,
                             const int32_t* parents, float* out, int B, int T, int Hq, int Hkv,
                             int D, int ctx, int bf16, float scale, void* workspace,
-                            hipStream_t st) {
-  AttnArgs a;
+                            hipStream_t st, const PagedKV* paged) {
+  AttnArgs a{};
   a.q = q; a.k = k; a.v = v; a.parents = parents; a.out = out;
   a.part_o = (float*)workspace;
   a.part_ml = (float*)((char*)workspace + p.part_o_bytes);
   a.B = B; a.T = T; a.Hq = Hq; a.Hkv = Hkv; a.G = Hq / Hkv; a.D = D; a.ctx = ctx;
   a.L = ctx + T; a.R = p.rows; a.S = p.splits; a.chunk = p.chunk;
   a.scale_log2 = scale * kLog2e;
+  (void)bf16;
   const dim3 grid(p.splits, B * Hkv, p.row_chunks);
-  if (p.mfma) {
-    if (D == 64) launch_mfma<64>(p, a, st, grid);
-    else launch_mfma<128>(p, a, st, grid);
+  if (paged != nullptr) {
+    const int64_t ps = paged->page_size;
+    a.block_table = paged->block_table;
+    a.ctx_lens = paged->ctx_lens;
+    a.page_shift = __builtin_ctz((unsigned)paged->page_size);
+    a.max_blocks = paged->max_blocks;
+    a.num_pages = paged->num_pages;
+    a.page_stride = ps * Hkv * D;
+    if (paged->position_major) {     // [pages, page_size, Hkv, D]
+      a.head_stride = D; a.row_stride = (int64_t)Hkv * D;
+    } else {                         // [pages, Hkv, page_size, D]
+      a.head_stride = ps * D; a.row_stride = D;
+    }
+    launch_main<true>(p, a, st, grid);
   } else {
-    if (D == 64) launch_valu<64>(p, a, st, grid);
-    else launch_valu<128>(p, a, st, grid);
+    launch_main<false>(p, a, st, grid);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || (p.mfma && p.splits == 1)) return e;

@@ -65,6 +65,16 @@ struct TreePlan {
   size_t part_bytes, total_bytes;
 };
 
+// A paged KV cache (see AttnArgs): position i of sequence b is row
+// i % page_size of page block_table[b][i / page_size].
+struct PagedKV {
+  const int32_t* block_table;  // [B, max_blocks]
+  const int32_t* ctx_lens;     // [B] or nullptr
+  int page_size;               // a power of two
+  int max_blocks, num_pages;
+  int position_major;          // 0: [pages, Hkv, page_size, D]; 1: [pages, page_size, Hkv, D]
+};
+
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 }  // namespace sv

@@ -12,7 +12,7 @@ AttnPlan plan_attention(int B, int T, int Hq, int Hkv, int D, int ctx, int bf16)
 hipError_t launch_attention(const AttnPlan& p, const void* q, const void* k, const void* v,
                             const int32_t* parents, float* out, int B, int T, int Hq, int Hkv,
                             int D, int ctx, int bf16, float scale, void* workspace,
-                            hipStream_t st);
+                            hipStream_t st, const PagedKV* paged);
 ChainPlan plan_chain(int B, int N, int V);
 hipError_t launch_chain(const ChainPlan& p, const float* target, const float* draft,
                         const int32_t* tokens, const float* u_acc, const float* u_draw,
@@ -89,7 +89,47 @@ spec_status spec_verify_attention(const void* q, const void* k, const void* v,
   if (workspace_bytes < p.total_bytes) return SPEC_ERR_WORKSPACE;
   const hipError_t e = sv::launch_attention(p, q, k, v, parents, out, B, T, Hq, Hkv, D, ctx,
                                             dtype == SPEC_BF16, scale, workspace,
-                                            (hipStream_t)hip_stream);
+                                            (hipStream_t)hip_stream, nullptr);
+  return e == hipSuccess ? SPEC_OK : SPEC_ERR_HIP;
+}
+
+size_t spec_verify_attention_paged_workspace(int B, int T, int Hq, int Hkv, int D, int max_ctx,
+                                             spec_dtype dtype) {
+  return spec_verify_attention_workspace(B, T, Hq, Hkv, D, max_ctx, dtype);
+}
+
+spec_status spec_verify_attention_paged(const void* q, const void* k_pages, const void* v_pages,
+                                        const int32_t* block_table, const int32_t* ctx_lens,
+                                        const int32_t* parents, float* out, int B, int T,
+                                        int Hq, int Hkv, int D, int max_ctx, int page_size,
+                                        int num_pages, int max_blocks, spec_page_layout layout,
+                                        spec_dtype dtype, float scale, void* workspace,
+                                        size_t workspace_bytes, void* hip_stream) {
+  const spec_status c = check_attention(B, T, Hq, Hkv, D, max_ctx, dtype);
+  if (c != SPEC_OK) return c;
+  if (!isfinite(scale) || !(scale > 0.f)) return SPEC_ERR_SHAPE;
+  if (page_size < 1 || num_pages < 1 || max_blocks < 1) return SPEC_ERR_SHAPE;
+  if ((page_size & (page_size - 1)) != 0 || page_size > SPEC_MAX_PAGE_SIZE)
+    return SPEC_ERR_UNSUPPORTED;
+  if (layout != SPEC_PAGES_HND && layout != SPEC_PAGES_NHD) return SPEC_ERR_UNSUPPORTED;
+  // the table must reach the longest sequence
+  if ((long long)max_blocks * page_size < (long long)max_ctx + T) return SPEC_ERR_SHAPE;
+  if (B == 0 || T == 0) return SPEC_OK;
+  if (!q || !k_pages || !v_pages || !block_table || !out || !workspace) return SPEC_ERR_NULL;
+  if (((uintptr_t)q | (uintptr_t)k_pages | (uintptr_t)v_pages | (uintptr_t)out) % 16 != 0)
+    return SPEC_ERR_UNSUPPORTED;
+  const sv::AttnPlan p = sv::plan_attention(B, T, Hq, Hkv, D, max_ctx, dtype == SPEC_BF16);
+  if (workspace_bytes < p.total_bytes) return SPEC_ERR_WORKSPACE;
+  sv::PagedKV pk;
+  pk.block_table = block_table;
+  pk.ctx_lens = ctx_lens;
+  pk.page_size = page_size;
+  pk.max_blocks = max_blocks;
+  pk.num_pages = num_pages;
+  pk.position_major = layout == SPEC_PAGES_NHD;
+  const hipError_t e = sv::launch_attention(p, q, k_pages, v_pages, parents, out, B, T, Hq, Hkv,
+                                            D, max_ctx, dtype == SPEC_BF16, scale, workspace,
+                                            (hipStream_t)hip_stream, &pk);
   return e == hipSuccess ? SPEC_OK : SPEC_ERR_HIP;
 }
 

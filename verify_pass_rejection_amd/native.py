@@ -18,6 +18,8 @@ _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libspecver
 
 SPEC_OK, SPEC_ERR_NULL, SPEC_ERR_SHAPE, SPEC_ERR_UNSUPPORTED, SPEC_ERR_WORKSPACE, SPEC_ERR_HIP = range(6)
 SPEC_F32, SPEC_BF16 = 0, 1
+SPEC_PAGES_HND, SPEC_PAGES_NHD = 0, 1
+_LAYOUTS = {"hnd": SPEC_PAGES_HND, "nhd": SPEC_PAGES_NHD}
 
 #: Every function the header declares, with its ctypes signature.
 _c = ctypes
@@ -26,6 +28,10 @@ _SIGNATURES = {
     "spec_verify_attention_workspace": (_c.c_size_t, [_c.c_int] * 6 + [_c.c_int]),
     "spec_verify_attention": (_c.c_int, [_c.c_void_p] * 5 + [_c.c_int] * 6 + [_c.c_int, _c.c_float,
                                         _c.c_void_p, _c.c_size_t, _c.c_void_p]),
+    "spec_verify_attention_paged_workspace": (_c.c_size_t, [_c.c_int] * 6 + [_c.c_int]),
+    "spec_verify_attention_paged": (_c.c_int, [_c.c_void_p] * 7 + [_c.c_int] * 9
+                                    + [_c.c_int, _c.c_int, _c.c_float,
+                                       _c.c_void_p, _c.c_size_t, _c.c_void_p]),
     "spec_accept_chain_workspace": (_c.c_size_t, [_c.c_int] * 3),
     "spec_accept_chain": (_c.c_int, [_c.c_void_p] * 5 + [_c.c_float] + [_c.c_void_p] * 2
                           + [_c.c_int] * 3 + [_c.c_void_p, _c.c_size_t, _c.c_void_p]),
@@ -140,6 +146,57 @@ def spec_verify_attention(q, k, v, ctx, parents=None, out=None, scale=None,
                                       B, T, Hq, Hkv, D, ctx, dt, float(scale),
                                       _ptr(ws), ws.numel() * ws.element_size(), _stream(stream))
     _raise(st, "spec_verify_attention")
+    return out
+
+
+def spec_verify_attention_paged_workspace(B, T, Hq, Hkv, D, max_ctx, dtype=SPEC_BF16) -> int:
+    return int(load().spec_verify_attention_paged_workspace(B, T, Hq, Hkv, D, max_ctx, dtype))
+
+
+def spec_verify_attention_paged(q, k_pages, v_pages, block_table, max_ctx, ctx_lens=None,
+                                parents=None, layout="hnd", out=None, scale=None,
+                                workspace=None, stream=None):
+    """out [B,T,Hq,D] fp32 = verify attention over a paged KV cache (see the header).
+
+    k_pages, v_pages: [P, Hkv, page_size, D] ("hnd") or [P, page_size, Hkv, D]
+    ("nhd"); block_table [B, max_blocks] int32; ctx_lens [B] int32 or None.
+    """
+    B, T, Hq, D = q.shape
+    dev = q.device
+    dt = {torch.float32: SPEC_F32, torch.bfloat16: SPEC_BF16}[q.dtype]
+    if layout not in _LAYOUTS:
+        raise ValueError(f"layout must be 'hnd' or 'nhd', not {layout!r}")
+    if k_pages.dim() != 4:
+        raise ValueError("k_pages must be 4-D")
+    P = k_pages.shape[0]
+    if layout == "hnd":
+        Hkv, ps = k_pages.shape[1], k_pages.shape[2]
+        pshape = (P, Hkv, ps, D)
+    else:
+        ps, Hkv = k_pages.shape[1], k_pages.shape[2]
+        pshape = (P, ps, Hkv, D)
+    _check(q, "q", (B, T, Hq, D), q.dtype, dev)
+    _check(k_pages, "k_pages", pshape, q.dtype, dev)
+    _check(v_pages, "v_pages", pshape, q.dtype, dev)
+    if block_table.dim() != 2:
+        raise ValueError("block_table must be [B, max_blocks]")
+    _check(block_table, "block_table", (B, block_table.shape[1]), torch.int32, dev)
+    if ctx_lens is not None:
+        _check(ctx_lens, "ctx_lens", (B,), torch.int32, dev)
+    if parents is not None:
+        _check(parents, "parents", (B, T), torch.int32, dev)
+    if out is None:
+        out = torch.empty((B, T, Hq, D), dtype=torch.float32, device=dev)
+    _check(out, "out", (B, T, Hq, D), torch.float32, dev)
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    need = spec_verify_attention_paged_workspace(B, T, Hq, Hkv, D, max_ctx, dt)
+    ws = _workspace(need, dev, workspace)
+    st = load().spec_verify_attention_paged(
+        _ptr(q), _ptr(k_pages), _ptr(v_pages), _ptr(block_table), _ptr(ctx_lens), _ptr(parents),
+        _ptr(out), B, T, Hq, Hkv, D, max_ctx, ps, P, block_table.shape[1], _LAYOUTS[layout], dt,
+        float(scale), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream))
+    _raise(st, "spec_verify_attention_paged")
     return out
 
 
