@@ -10,7 +10,9 @@ Printed: one JSON line with the step time, the achieved algorithmic HBM
 bandwidth of the step, of attention and of acceptance, the per-position
 verification overhead α = (T(N) − T(0)) / (N·T(0)) at N = 4 and 8 on the same
 shape, a roofline entry for the attention kernel and the CPU oracle's rate on a
-bounded sample of the same workload.
+bounded sample of the same workload.  Beside the line's own figures: the
+attention call over a paged copy of the same cache (pages of 16 positions),
+and for trees the KV commit of the accepted path.
 """
 from __future__ import annotations
 
@@ -171,6 +173,51 @@ def time_commit(step, steps: int):
             "note": "latency-bound: a few hundred KB per call"}
 
 
+def time_paged(step, steps: int, flush=None, page_size: int = 16, layout: str = "hnd"):
+    """Attention over a paged copy of the same cache (spec_verify_attention_paged:
+    pages of page_size positions in a shuffled pool, every prefix at ctx) and
+    the contiguous call, each timed per call with events in 3 interleaved
+    rounds (median of the round medians); the two outputs must be
+    bit-identical."""
+    import torch
+    from verify_pass_rejection_amd import inputs as I
+    w, nat = step.w, step.nat
+    kp, vp, bt = I.make_paged_kv(w, step.k, step.v, page_size, layout)
+    out = torch.empty_like(step.out)
+
+    def paged():
+        nat.spec_verify_attention_paged(step.q, kp, vp, bt, w.ctx, parents=step.parents,
+                                        layout=layout, out=out, workspace=step.ws_a)
+
+    def per_call(fn, n):
+        for _ in range(2):
+            fn()
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(n)]
+        for i in range(n):
+            if flush is not None:
+                flush.zero_()
+            ev[i][0].record()
+            fn()
+            ev[i][1].record()
+        torch.cuda.synchronize()
+        return pct([a.elapsed_time(b) for a, b in ev], 0.5)
+
+    rounds = {"paged": [], "contiguous": []}
+    for _ in range(3):
+        rounds["contiguous"].append(per_call(step.attention, max(10, steps // 3)))
+        rounds["paged"].append(per_call(paged, max(10, steps // 3)))
+    same = bool(torch.equal(out, step.out))
+    del kp, vp, bt
+    torch.cuda.empty_cache()
+    ab = attention_bytes(w)
+    us = pct(rounds["paged"], 0.5) * 1e3
+    us_c = pct(rounds["contiguous"], 0.5) * 1e3
+    return {"page_size": page_size, "layout": layout, "us": round(us, 2),
+            "GBps": round(ab / (us * 1e-6) / 1e9, 1),
+            "frac_hbm_peak": round(ab / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
+            "contiguous_us": round(us_c, 2), "bitwise_equal_to_contiguous": same}
+
+
 def cpu_baseline(w, step, budget_s: float = 30.0):
     """The fp64 oracle on a bounded sample: sequence 0 of the same batch
     (attention for all its heads and positions, then its acceptance)."""
@@ -255,6 +302,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-alpha", action="store_true")
+    ap.add_argument("--no-paged", action="store_true",
+                    help="skip the paged-KV attention timing")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (for scaling byte counters)")
     ap.add_argument("--workload", default=WORKLOAD,
@@ -309,6 +358,8 @@ def main():
         alphas = {f"alpha_N{n}": round(alpha(times[n], times[0], n), 4) for n in ns if n > 0}
         alphas["verify_step_us_by_N"] = {str(n): round(times[n] * 1e3, 2) for n in ns}
 
+    paged = None if args.no_paged else time_paged(step, args.steps, flush)
+
     commit = None
     if w.kind == "tree":
         commit = time_commit(step, args.steps)
@@ -354,6 +405,8 @@ def main():
                      "algorithmic_bytes_per_launch": ab},
         "cpu_baseline": cpu,
     }
+    if paged is not None:
+        line["paged_attention"] = paged
     if commit is not None:
         line["kv_commit"] = commit
     print(json.dumps(line), flush=True)
