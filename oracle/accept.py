@@ -22,6 +22,10 @@ engine commits to the target's own choice at the first divergence.  The check
 is greedy (the mc2informatique article, step 2: do the drafts match the target's
 own predictions).
 
+Sampled tree (``tree_accept_sampled``) — the §9.1 rule applied to the several
+candidates a tree offers for the same position, one after the other (its
+docstring lists the readings).
+
 Readings where the pages are silent:
 
 * the ratio test is ``u < r`` with caller uniforms u in (0, 1); one u_accept per
@@ -204,3 +208,111 @@ def tree_accept(target_logits, tokens, parents) -> TreeResult:
         emitted = [int(tok[b, n]) for n in nodes[1:]] + [int(choice[b, best])]
         out[b, :len(emitted)] = emitted
     return TreeResult(accept_len, path, out)
+
+
+#: Relative error bound assumed for the probabilities of an implementation
+#: that takes the sampled-tree decisions in float64 from exponentials rounded
+#: to float32 (each p(v), q(v) within this factor of the exact value).
+PROB_REL_ERR = 1e-6
+
+
+@dataclass
+class SampledTreeResult:
+    accept_len: np.ndarray     # [B] int32: depth of the last accepted node
+    path: np.ndarray           # [B, T] int32: node ids root..last, then -1
+    out_tokens: np.ndarray     # [B, T] int32: path tokens (root excluded) + the drawn token, then -1
+    near_boundary: np.ndarray  # [B] bool: some used decision lies within the error band
+
+
+def tree_children(parents_row, T: int) -> list[list[int]]:
+    """Children of every node in increasing id order; a node whose parent is
+    not in [0, id) is nobody's child."""
+    kids: list[list[int]] = [[] for _ in range(T)]
+    for i in range(1, T):
+        pa = int(parents_row[i])
+        if 0 <= pa < i:
+            kids[pa].append(i)
+    return kids
+
+
+def tree_accept_sampled(target_logits, draft_logits, tokens, parents, u_accept, u_draw,
+                        temperature: float = 1.0, band: float = BOUNDARY_BAND,
+                        eta: float = PROB_REL_ERR) -> SampledTreeResult:
+    """Sampled (non-greedy) verification of a draft tree, per sequence.
+
+    The Primer §9.2 has the target pick the best of several draft paths and
+    §9.1 gives the one-candidate rule: keep a draft x with probability
+    min(1, p(x)/q(x)), otherwise draw from the normalised (p - q)+.  With
+    several candidates for the same position the rule is applied to them one
+    after the other.  Readings (the pages give no multi-candidate rule):
+
+    * the children of node n are the candidates for the token after n; they
+      were drawn independently (with replacement) from q_n = softmax of
+      draft_logits[b, n]; p_n = softmax of target_logits[b, n];
+    * at node n the reference distribution starts as p_n; the children are
+      tried in increasing id order; child i is kept iff u_accept[b, i] <
+      ref(x_i) / q_n(x_i) (q = 0: +inf if ref(x) > 0, else 0; a token outside
+      [0, V) gives 0); after each rejection ref becomes the normalised
+      (ref - q_n)+ (a residual summing to zero falls back to p_n);
+    * a kept child becomes the current node and the walk goes on from it;
+    * when no child is kept (a leaf, or every child rejected) the emitted
+      token is drawn from ref with u_draw[b, n] (``inverse_cdf``).
+
+    Flags: a ratio test or a draw edge is flagged when its uniform lies within
+    band (relative) plus the first-order error that probabilities accurate to
+    ``eta`` (relative) can cause in that quantity; the residual is tracked as
+    (p - c q)+ / Z for that bound only.
+    """
+    zp = np.asarray(target_logits)
+    zq = np.asarray(draft_logits)
+    B, T, V = zp.shape
+    assert zq.shape == (B, T, V)
+    tok = np.asarray(tokens, dtype=np.int64).reshape(B, T)
+    par = np.asarray(parents, dtype=np.int64).reshape(B, T)
+    ua = np.asarray(u_accept, dtype=np.float64).reshape(B, T)
+    ud = np.asarray(u_draw, dtype=np.float64).reshape(B, T)
+    accept_len = np.zeros(B, dtype=np.int32)
+    path = np.full((B, T), -1, dtype=np.int32)
+    out = np.full((B, T), -1, dtype=np.int32)
+    flag = np.zeros(B, dtype=bool)
+    for b in range(B):
+        kids = tree_children(par[b], T)
+        n, nodes = 0, [0]
+        while True:
+            p = softmax(zp[b, n], temperature)
+            q = softmax(zq[b, n], temperature)
+            ref, c, Z = p.copy(), 0.0, 1.0
+            kept = None
+            for ch in kids[n]:
+                x = int(tok[b, ch])
+                if 0 <= x < V:
+                    px, qx, rx = p[x], q[x], ref[x]
+                    r = rx / qx if qx > 0 else (np.inf if rx > 0 else 0.0)
+                else:
+                    px = qx = rx = r = 0.0
+                if np.isfinite(r) and qx > 0:
+                    err = eta * ((px + c * qx) / (Z * qx) + r * ((1.0 + c) / Z + 1.0))
+                    flag[b] |= abs(ua[b, ch] - r) <= band * r + err
+                if ua[b, ch] < r:
+                    kept = ch
+                    break
+                new = np.maximum(ref - q, 0.0)
+                s = new.sum()
+                if s > 0:
+                    ref = new / s
+                    c, Z = c + Z, Z * s
+                else:
+                    ref, c, Z = p.copy(), 0.0, 1.0
+            if kept is None:
+                break
+            nodes.append(kept)
+            n = kept
+        u = ud[b, n]
+        y, lo, hi = inverse_cdf(ref, u)
+        err = 2.0 * eta * (1.0 + c) / Z
+        flag[b] |= (abs(u - lo) <= band * lo + err) | (abs(u - hi) <= band * hi + err)
+        accept_len[b] = len(nodes) - 1
+        path[b, :len(nodes)] = nodes
+        emitted = [int(tok[b, i]) for i in nodes[1:]] + [int(y)]
+        out[b, :len(emitted)] = emitted
+    return SampledTreeResult(accept_len, path, out, flag)

@@ -27,7 +27,7 @@ import torch
 # Named substreams: a per-input offset added to the workload seed.
 _STREAMS = {"q": 1, "k": 2, "v": 3, "target": 4, "draft_noise": 5,
             "draft_gumbel": 6, "u_accept": 7, "u_draw": 8, "tree": 9,
-            "tree_tokens": 10, "ctx_lens": 11, "pages": 12}
+            "tree_tokens": 10, "ctx_lens": 11, "pages": 12, "stree_gumbel": 13}
 
 #: Spike written into a parent's logit row at the planted child's token, in
 #: units of the logit standard deviation (8σ is never reached by N(0, σ²)
@@ -239,6 +239,38 @@ def make_tree_inputs(w: Workload, device="cpu"):
                     tokens[b, c] = int(torch.randint(0, V, (1,), generator=gk))
     return dict(target_logits=logits, tokens=tokens.to(torch.int32).to(device),
                 parents=parents.to(device))
+
+
+def make_sampled_tree_inputs(w: Workload, device="cpu", draft_noise_sd: float = 1.0):
+    """Inputs for sampled (non-greedy) tree acceptance.
+
+    parents: as make_tree_inputs (eagle2 / medusa shapes); target logits
+    [B, T, V] ~ N(0, target_sd²); draft logits = target + N(0, draft_noise_sd²)
+    (row n is the draft's distribution for node n's children); each node's
+    token is drawn from its parent's draft row by Gumbel-max (independently,
+    so siblings may repeat a token); u_accept and u_draw [B, T] uniforms.
+    """
+    B, T, V = w.B, w.T, w.V
+    parents = make_tree_inputs(w.with_(V=8), "cpu")["parents"]
+    target = _normal((B, T, V), _gen(w, "target", device), device, torch.float32,
+                     sd=w.target_sd)
+    noise = _normal((B, T, V), _gen(w, "draft_noise", device), device, torch.float32,
+                    sd=draft_noise_sd)
+    draft = target + noise
+    del noise
+    par = parents.to(device).long()
+    g = _gen(w, "stree_gumbel", device)
+    tokens = torch.zeros((B, T), dtype=torch.int64, device=device)
+    for b in range(B):
+        # one Gumbel row per node, added to its parent's draft row
+        gu = uniforms((T, V), g, device).double()
+        rows = draft[b, par[b].clamp(min=0)].double() / w.temperature
+        tokens[b] = torch.argmax(rows - torch.log(-torch.log(gu)), dim=-1)
+    tokens[:, 0] = 0
+    return dict(target_logits=target, draft_logits=draft.contiguous(),
+                tokens=tokens.to(torch.int32), parents=par.to(torch.int32),
+                u_accept=uniforms((B, T), _gen(w, "u_accept", device), device),
+                u_draw=uniforms((B, T), _gen(w, "u_draw", device), device))
 
 
 def ragged_ctx_lens(w: Workload, device="cpu") -> torch.Tensor:
