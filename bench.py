@@ -12,7 +12,8 @@ verification overhead α = (T(N) − T(0)) / (N·T(0)) at N = 4 and 8 on the sam
 shape, a roofline entry for the attention kernel and the CPU oracle's rate on a
 bounded sample of the same workload.  Beside the line's own figures: the
 attention call over a paged copy of the same cache (pages of 16 positions),
-and for trees the KV commit of the accepted path.
+and for trees the KV commit of the accepted path and the sampled (non-greedy)
+acceptance of the same tree shape.
 """
 from __future__ import annotations
 
@@ -218,6 +219,46 @@ def time_paged(step, steps: int, flush=None, page_size: int = 16, layout: str = 
             "contiguous_us": round(us_c, 2), "bitwise_equal_to_contiguous": same}
 
 
+def time_sampled_tree(w, dev, steps: int, flush=None):
+    """spec_accept_tree_sampled on the same tree shape with draft rows (draft
+    logits = target + N(0, 1) noise, children drawn from their parent's q),
+    timed per call with events; flush as for the step.  Bytes of the
+    statistics pass: every target row and the draft row of every node with
+    children, once."""
+    import torch
+    from verify_pass_rejection_amd import inputs as I
+    from verify_pass_rejection_amd import native as nat
+    d = I.make_sampled_tree_inputs(w, dev)
+    args = (d["target_logits"], d["draft_logits"], d["tokens"], d["parents"], d["u_accept"],
+            d["u_draw"])
+    al, path, out = nat.spec_accept_tree_sampled(*args)
+    ws = torch.empty(max(1, nat.spec_accept_tree_sampled_workspace(w.B, w.T, w.V)),
+                     dtype=torch.uint8, device=dev)
+    run = lambda: nat.spec_accept_tree_sampled(*args, accept_len=al, path=path,  # noqa: E731
+                                               out_tokens=out, workspace=ws)
+    for _ in range(3):
+        run()
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
+    for i in range(steps):
+        if flush is not None:
+            flush.zero_()
+        ev[i][0].record()
+        run()
+        ev[i][1].record()
+    torch.cuda.synchronize()
+    ts = [a.elapsed_time(b) * 1e3 for a, b in ev]
+    par = d["parents"].cpu()
+    internal = sum(len(set(int(x) for x in par[b, 1:].tolist() if x >= 0)) for b in range(w.B))
+    stats_bytes = (w.B * w.T + internal) * w.V * 4
+    us = pct(ts, 0.5)
+    return {"us": round(us, 2), "us_p10_p50_p90": [round(pct(ts, q), 2) for q in (0.1, 0.5, 0.9)],
+            "mean_accepted": round(float(al.float().mean()), 3),
+            "statistics_pass_bytes": stats_bytes,
+            "note": "one block per sequence walks the tree; latency-bound beyond the "
+                    "statistics pass"}
+
+
 def cpu_baseline(w, step, budget_s: float = 30.0):
     """The fp64 oracle on a bounded sample: sequence 0 of the same batch
     (attention for all its heads and positions, then its acceptance)."""
@@ -360,9 +401,10 @@ def main():
 
     paged = None if args.no_paged else time_paged(step, args.steps, flush)
 
-    commit = None
+    commit = sampled = None
     if w.kind == "tree":
         commit = time_commit(step, args.steps)
+        sampled = time_sampled_tree(w, dev, args.steps, flush)
 
     cpu = None
     if not args.no_cpu_baseline and w.kind == "chain":
@@ -409,6 +451,8 @@ def main():
         line["paged_attention"] = paged
     if commit is not None:
         line["kv_commit"] = commit
+    if sampled is not None:
+        line["sampled_tree_acceptance"] = sampled
     print(json.dumps(line), flush=True)
 
 

@@ -217,6 +217,49 @@ spec_status spec_accept_tree(const float* target_logits, const int32_t* tokens,
                              void* workspace, size_t workspace_bytes, void* hip_stream);
 
 /* ---------------------------------------------------------------------------
+ * Sampled (non-greedy) tree acceptance (Primer §9.1: keep a draft x with
+ * probability min(1, p(x)/q(x)), else draw from the normalised (p − q)+, which
+ * keeps the output distributed as the target's own sampling; Primer §9.2: the
+ * target picks among several draft paths).
+ *
+ * p_n = softmax(target_logits[b,n,:] / temperature) and q_n =
+ * softmax(draft_logits[b,n,:] / temperature); the children of node n are
+ * candidates for the token after n, drawn independently from q_n.  The walk
+ * starts at the root with ref = p_0.  At node n the children are tried in
+ * increasing id order: child i (token x_i) is kept iff u_accept[b,i] <
+ * ref(x_i) / q_n(x_i) (q = 0: +inf if ref(x) > 0, else 0; a token outside
+ * [0, V) gives 0), and the walk moves to it with ref = p_i; after a rejection
+ * ref becomes the normalised (ref − q_n)+ (p_n if that is empty).  When no
+ * child of the current node l is kept, the emitted token y is drawn from ref
+ * with u_draw[b,l]: y = min{j : C_j > u·C_{V-1}} over the running sum C of
+ * ref in ascending token order (among tokens with positive weight).
+ *
+ *   target_logits, draft_logits  [B, T, V] float32 (row n of draft_logits is
+ *                                the distribution node n's children came from)
+ *   tokens         [B, T] int32 (node 0 ignored)
+ *   parents        [B, T] int32, parents[b][0] = -1, parents[b][i] < i
+ *   u_accept       [B, T] float32 in (0,1), node i's own ratio test (node 0 unused)
+ *   u_draw         [B, T] float32 in (0,1), used at the node where the walk stops
+ *   temperature    > 0
+ *   accept_len     [B] int32 out: depth of l (number of kept drafts)
+ *   path           [B, T] int32 out: node ids root..l, then -1
+ *   out_tokens     [B, T] int32 out: tokens of path nodes 1..l, then y, then -1
+ *
+ * Precision: probabilities from float32-accurate exponentials (an exact
+ * float64 argument split around the hardware exp2), every sum, ratio and
+ * comparison in float64.  Limits: 1 <= T <= 64, 1 <= V <= SPEC_MAX_V.
+ * ------------------------------------------------------------------------- */
+size_t spec_accept_tree_sampled_workspace(int B, int T, int V);
+
+spec_status spec_accept_tree_sampled(const float* target_logits, const float* draft_logits,
+                                     const int32_t* tokens, const int32_t* parents,
+                                     const float* u_accept, const float* u_draw,
+                                     float temperature, int32_t* accept_len, int32_t* path,
+                                     int32_t* out_tokens, int B, int T, int V,
+                                     void* workspace, size_t workspace_bytes,
+                                     void* hip_stream);
+
+/* ---------------------------------------------------------------------------
  * KV commit after acceptance (Primer §9.1: at the first divergence the engine
  * commits to the target's choice and drops the rest; glossary "Limites du
  * parallel decoding": tree attention keeps every branch's keys and values in

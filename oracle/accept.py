@@ -260,8 +260,9 @@ def tree_accept_sampled(target_logits, draft_logits, tokens, parents, u_accept, 
 
     Flags: a ratio test or a draw edge is flagged when its uniform lies within
     band (relative) plus the first-order error that probabilities accurate to
-    ``eta`` (relative) can cause in that quantity; the residual is tracked as
-    (p - c q)+ / Z for that bound only.
+    ``eta`` (relative) can cause in that quantity, and a residual whose mass is
+    within that error of zero is flagged (the emptiness test is a decision
+    too); the residual is tracked as (p - c q)+ / Z for these bounds only.
     """
     zp = np.asarray(target_logits)
     zq = np.asarray(draft_logits)
@@ -301,6 +302,8 @@ def tree_accept_sampled(target_logits, draft_logits, tokens, parents, u_accept, 
                 if s > 0:
                     ref = new / s
                     c, Z = c + Z, Z * s
+                    # an implementation may find a residual this small empty
+                    flag[b] |= Z <= 2.0 * eta * (1.0 + c)
                 else:
                     ref, c, Z = p.copy(), 0.0, 1.0
             if kept is None:

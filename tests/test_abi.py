@@ -25,7 +25,7 @@ def declared_functions():
 def test_library_loads_and_exports_every_declared_symbol():
     lib = nat.load()
     decl = declared_functions()
-    assert len(decl) == 10
+    assert len(decl) == 12
     for name in decl:
         assert hasattr(lib, name), name
     assert sorted(nat.exported_symbols()) == decl
@@ -185,6 +185,37 @@ def commit(**kw):
     a.update(kw)
     return nat.load().spec_commit_kv(a["k"], a["v"], a["path"], a["acc"], a["new_len"], a["B"],
                                      a["T"], a["Hkv"], a["D"], a["ctx"], a["dtype"], a["stream"])
+
+
+def stree(**kw):
+    a = dict(t=FAKE, d=FAKE, x=FAKE, par=FAKE, ua=FAKE, ud=FAKE, tau=1.0, al=FAKE, path=FAKE,
+             out=FAKE, B=4, T=8, V=1000, ws=FAKE, ws_bytes=1 << 40, stream=None)
+    a.update(kw)
+    return nat.load().spec_accept_tree_sampled(a["t"], a["d"], a["x"], a["par"], a["ua"],
+                                               a["ud"], a["tau"], a["al"], a["path"],
+                                               a["out"], a["B"], a["T"], a["V"], a["ws"],
+                                               a["ws_bytes"], a["stream"])
+
+
+def test_sampled_tree_validation():
+    assert stree(t=None) == NULL
+    assert stree(d=None) == NULL
+    assert stree(ua=None) == NULL
+    assert stree(ud=None) == NULL
+    assert stree(path=None) == NULL
+    assert stree(tau=0.0) == SHAPE
+    assert stree(tau=float("inf")) == SHAPE
+    assert stree(B=-1) == SHAPE
+    assert stree(V=0) == SHAPE
+    assert stree(T=65) == UNSUP
+    assert stree(V=(1 << 24) + 1) == UNSUP
+    assert stree(ws=None) == NULL
+    assert stree(ws_bytes=8) == WS
+    assert stree(B=0, t=None) == OK
+    assert stree(T=0, t=None) == OK
+    f = nat.spec_accept_tree_sampled_workspace
+    assert f(8, 64, 32000) >= 2 * 8 * 64 * 4 * 12 and f(8, 64, 32000) % 256 == 0
+    assert f(0, 64, 32000) == 0 and f(8, 65, 32000) == 0
 
 
 def test_commit_validation():

@@ -1,0 +1,132 @@
+"""GPU parity of spec_accept_tree_sampled against oracle.accept.tree_accept_sampled.
+
+Accepted lengths, paths and emitted tokens must match the oracle exactly on
+every sequence whose decisions are not flagged.  The kernel takes its
+decisions in float64 from probabilities accurate to about 2 float32 ulp; the
+oracle flags a decision when its uniform lies within the band 1e-6 (relative)
+plus the error that probabilities within PROB_REL_ERR (1e-6, relative) can
+cause in the tested quantity.  Flag counts are printed.  A χ² law test runs
+the kernel itself on 2·10^5 sampled trees.
+"""
+import numpy as np
+import pytest
+import torch
+from scipy import stats
+from scipy.special import softmax as sp_softmax
+
+from gpu_support import device, f64, i64, say
+from oracle.accept import tree_accept_sampled
+from verify_pass_rejection_amd import inputs as I
+from verify_pass_rejection_amd import native as nat
+
+pytestmark = pytest.mark.gpu
+
+TEST_BAND = 1e-6
+
+
+def compare(d, temperature=1.0, label=""):
+    al, path, out = nat.spec_accept_tree_sampled(
+        d["target_logits"], d["draft_logits"], d["tokens"], d["parents"], d["u_accept"],
+        d["u_draw"], temperature=temperature)
+    torch.cuda.synchronize()
+    ref = tree_accept_sampled(f64(d["target_logits"]), f64(d["draft_logits"]), i64(d["tokens"]),
+                              i64(d["parents"]), f64(d["u_accept"]), f64(d["u_draw"]),
+                              temperature=temperature, band=TEST_BAND)
+    al, path, out = i64(al), i64(path), i64(out)
+    ok = ~ref.near_boundary
+    mism = ok & ((al != ref.accept_len) | np.any(path != ref.path, axis=1)
+                 | np.any(out != ref.out_tokens, axis=1))
+    say(label, f"B={len(al)} flagged={int((~ok).sum())} mismatched={int(mism.sum())}",
+        f"mean_accepted={al.mean():.3f}")
+    assert not mism.any(), np.nonzero(mism)[0][:10]
+    assert (~ok).mean() < 0.15
+    # what the oracle does not fix on flagged sequences is still well formed
+    for b in range(len(al)):
+        n = al[b]
+        assert path[b, 0] == 0 and np.all(path[b, n + 1:] == -1) and np.all(out[b, n + 1:] == -1)
+        assert 0 <= out[b, n] < d["target_logits"].shape[2]
+    return al, path, out
+
+
+@pytest.mark.parametrize("name,kw", [
+    ("eagle2_tree", dict(B=4, V=4000)),
+    ("medusa70b_tree", dict(B=6, V=3001)),          # V not a multiple of 4
+    ("eagle2_tree", dict(B=64, V=777)),              # many sequences, chunks of one token
+    ("eagle2_tree", dict()),                         # full reference size
+    ("medusa70b_tree", dict()),                      # full reference size
+])
+def test_matches_oracle(name, kw):
+    dev = device()
+    w = I.WORKLOADS[name].with_(**kw)
+    compare(I.make_sampled_tree_inputs(w, dev), label=f"{name} {kw}")
+
+
+def test_temperature_and_close_drafts():
+    dev = device()
+    w = I.WORKLOADS["eagle2_tree"].with_(B=16, V=2000, seed=41)
+    compare(I.make_sampled_tree_inputs(w, dev, draft_noise_sd=0.3), temperature=0.7,
+            label="tau=0.7 noise=0.3")
+
+
+def test_root_only_leaf_and_edge_inputs():
+    dev = device()
+    # T = 1: the root is a leaf, plain inverse-CDF sampling from p_0
+    w = I.WORKLOADS["eagle2_tree"].with_(B=32, V=1000, seed=42)
+    d = I.make_sampled_tree_inputs(w, dev)
+    d1 = {k: (v[:, :1].contiguous() if v.dim() >= 2 else v) for k, v in d.items()}
+    al, path, out = compare(d1, label="T=1")
+    assert np.all(al == 0)
+    # invalid tokens, a malformed parent and q = p (a valid child is always kept)
+    d2 = dict(d)
+    d2["draft_logits"] = d["target_logits"].clone()
+    tok = d["tokens"].clone()
+    tok[:, 1] = -3
+    tok[:, 2] = w.V
+    par = d["parents"].clone()
+    par[:, 5] = 9                                   # points forward: never visited
+    d2["tokens"], d2["parents"] = tok, par
+    compare(d2, label="edge inputs")
+    # V = 1: every draft is token 0 and is kept
+    w1 = w.with_(V=1, B=4, seed=43)
+    compare(I.make_sampled_tree_inputs(w1, dev), label="V=1")
+
+
+def test_deterministic_run_twice():
+    dev = device()
+    d = I.make_sampled_tree_inputs(I.WORKLOADS["medusa70b_tree"].with_(B=8, V=5000), dev)
+    args = (d["target_logits"], d["draft_logits"], d["tokens"], d["parents"], d["u_accept"],
+            d["u_draw"])
+    a = [t.clone() for t in nat.spec_accept_tree_sampled(*args)]
+    b = nat.spec_accept_tree_sampled(*args)
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)
+
+
+def test_law_chi2_on_gpu():
+    dev = device()
+    V, trials = 6, 200_000
+    parents = torch.tensor([-1, 0, 0, 0, 1, 1, 2, 2], dtype=torch.int32)
+    T = len(parents)
+    g = torch.Generator(device=dev).manual_seed(91)
+    zp = torch.randn((T, V), generator=g, device=dev) * 1.5
+    zq = torch.randn((T, V), generator=g, device=dev) * 1.5
+    q = torch.softmax(zq.double(), -1)
+    tok = torch.zeros((trials, T), dtype=torch.int32, device=dev)
+    for i in range(1, T):
+        tok[:, i] = torch.multinomial(q[int(parents[i])], trials, replacement=True,
+                                      generator=g).to(torch.int32)
+    al, path, out = nat.spec_accept_tree_sampled(
+        zp.expand(trials, -1, -1).contiguous(), zq.expand(trials, -1, -1).contiguous(), tok,
+        parents.to(dev).expand(trials, -1).contiguous(), I.uniforms((trials, T), g, dev),
+        I.uniforms((trials, T), g, dev))
+    p = sp_softmax(f64(zp), axis=-1)
+    out, path = i64(out), i64(path)
+    crit = stats.chi2.ppf(0.999, V - 1)
+    chi = stats.chisquare(np.bincount(out[:, 0], minlength=V), trials * p[0]).statistic
+    say(f"chi2(first token vs p_root) = {chi:.2f} (df={V - 1}, 0.999 quantile {crit:.2f})")
+    assert chi < crit
+    for a in (1, 2):
+        sel = path[:, 1] == a
+        chi = stats.chisquare(np.bincount(out[sel, 1], minlength=V), sel.sum() * p[a]).statistic
+        say(f"chi2(token after node {a} vs p_{a}) = {chi:.2f} over {int(sel.sum())} trials")
+        assert chi < crit

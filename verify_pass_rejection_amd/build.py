@@ -15,7 +15,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libspecverify.so")
-SOURCES = ["attention.hip", "accept_chain.hip", "accept_tree.hip", "commit.hip", "spec_verify.cpp"]
+SOURCES = ["attention.hip", "accept_chain.hip", "accept_tree.hip", "accept_tree_sampled.hip",
+           "commit.hip", "spec_verify.cpp"]
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

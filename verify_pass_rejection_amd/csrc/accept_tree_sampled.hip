@@ -1,0 +1,464 @@
+// Sampled (non-greedy) acceptance of a draft tree.
+//
+// "LLM Primer VI — Chapitre 9 — Décodage spéculatif", §9.1: a draft x is kept
+// with probability min(1, p(x)/q(x)); otherwise the committed token is drawn
+// from the normalised (p − q)+, which keeps the output distributed as the
+// target's own sampling.  §9.2: the target picks among several draft paths (an
+// EAGLE-2 tree).  A node's children are several candidates for the same
+// position, drawn independently from that node's draft distribution q; they
+// are tried in increasing id order, each against the residual that the
+// rejections before it leave; when none is kept (or the node is a leaf) the
+// token is drawn from that residual.
+//
+// Two kernels:
+//  stree_stats — the whole chip, once over the logits: per 8192-logit chunk
+//                of every target row, and of the draft row of every node with
+//                children, the maximum and Σ 2^((z − max)·log2e/τ);
+//  stree_walk  — one 512-thread block per sequence.  It merges the chunk
+//                statistics of every node and gathers, for every node, p and
+//                q of its parent at its own token, so a ratio test is a few
+//                LDS reads.  A node's rows are read only when a rejection
+//                there needs the residual mass, or for the final draw: after j
+//                rejections the residual is (p − c_j q)+ / Z_j, with c_0 = 0,
+//                Z_0 = 1, c_{j+1} = c_j + Z_j and Z_{j+1} = Σ_v (p(v) −
+//                c_{j+1} q(v))+ (one pass per rejection).  For V <= 32768 the
+//                rows, once read, stay on chip while the node is visited: the
+//                target row in registers (up to 64 tokens per thread), the
+//                draft row in LDS.  The draw: each thread sums a contiguous
+//                chunk of the weights, a block scan gives every chunk its
+//                starting mass, each thread looks for the crossing in its own
+//                chunk and a block minimum picks the token.
+// Every reduction runs in a fixed order and leaves the same value in every
+// thread, so the walk's control flow is uniform without broadcasts.
+//
+// Precision: the probabilities a ratio test reads come from the hardware exp2
+// on an exact float64 argument split (2^a = 2^n · 2^f, n integer, |f| ≤ 1/2),
+// within about 2 ulp of float32; the row sums (normalisers, residual masses,
+// the draw) take float32 arguments (e_bulk); every sum, ratio and comparison
+// is float64.
+
+#include "common.h"
+
+// Products are rounded before they are subtracted: with q = p (identical rows)
+// the residual p − c q must cancel to exactly zero, which a fused multiply-add
+// of an unrounded c·q against the rounded p does not give.
+#pragma clang fp contract(off)
+
+namespace sv {
+
+struct STreeArgs {
+  const float* target;     // [B, T, V]
+  const float* draft;      // [B, T, V]
+  const int32_t* tokens;   // [B, T]
+  const int32_t* parents;  // [B, T]
+  const float* u_accept;   // [B, T]
+  const float* u_draw;     // [B, T]
+  int32_t* accept_len;     // [B]
+  int32_t* path;           // [B, T]
+  int32_t* out;            // [B, T]
+  float* part_m;           // [2, B*T, nchunks] chunk maxima (target rows, then draft rows)
+  double* part_s;          // [2, B*T, nchunks] chunk sums
+  int B, T, V, nchunks;
+  double k2;               // log2(e) / temperature
+  float k2f;               // the same, rounded to float32
+};
+
+constexpr int kSTThreads = 512;
+constexpr int kSTWaves = kSTThreads / kWave;
+constexpr int kSTChunk = 8192;                 // logits per statistics block
+
+// 2^a for a <= 0 (0 below the double range, or for z = -inf); branch-free.
+__device__ __forceinline__ double exp2_split(double a) {
+  const double ac = fmax(a, -1020.0);          // also maps -inf to a finite value
+  const double n = rint(ac);
+  const float f = (float)(ac - n);
+  const double r = ldexp((double)__builtin_amdgcn_exp2f(f), (int)n);
+  return a > -1020.0 ? r : 0.0;
+}
+
+// e(v) = 2^((z(v) − m)·k2) for the tokens a ratio test reads: float64
+// argument, float32 result (exact but below float32's range: 2^f is a float32
+// and 2^n a power of two), within about 2 ulp.
+__device__ __forceinline__ double e_of(float z, float m, double k2) {
+  return (double)(float)exp2_split(((double)z - m) * k2);
+}
+// The same for the sums over a whole row (normalisers, residual masses, the
+// draw): float32 argument and hardware exp2.  The argument's rounding adds
+// |a|·2^-24 (relative) to a term 2^a; a term with |a| >= 16 is below 2^-16 of
+// the row's largest, so the mass-weighted error of a sum stays below about
+// 1e-6 for V <= 2^20.
+__device__ __forceinline__ float e_bulk(float z, float m, float k2f) {
+  return __builtin_amdgcn_exp2f((z - m) * k2f);
+}
+
+// Block reductions: fixed order, the same result in every thread.
+__device__ __forceinline__ double block_sum(double x, double* red) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o);
+  __syncthreads();                       // red is free again
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = x;
+  __syncthreads();
+  double s = 0.0;
+#pragma unroll
+  for (int w = 0; w < kSTWaves; ++w) s += red[w];
+  return s;
+}
+__device__ __forceinline__ float block_max(float x, float* redf) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) x = fmaxf(x, __shfl_xor(x, o));
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) redf[threadIdx.x >> 6] = x;
+  __syncthreads();
+  float m = redf[0];
+#pragma unroll
+  for (int w = 1; w < kSTWaves; ++w) m = fmaxf(m, redf[w]);
+  return m;
+}
+__device__ __forceinline__ int block_min(int x, int* redi) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) x = min(x, __shfl_xor(x, o));
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) redi[threadIdx.x >> 6] = x;
+  __syncthreads();
+  int m = redi[0];
+#pragma unroll
+  for (int w = 1; w < kSTWaves; ++w) m = min(m, redi[w]);
+  return m;
+}
+
+// Marks cached row registers as rewritten, so that values derived from them
+// (float64 conversions, products) are recomputed in the pass that follows
+// instead of being kept alive across passes: the row already takes CH
+// registers, its float64 image would take 2·CH more.
+template <int N>
+__device__ __forceinline__ void launder(float (&r)[N]) {
+#pragma unroll
+  for (int i = 0; i < N; ++i) asm volatile("" : "+v"(r[i]));
+}
+
+// ---------------------------------------------------------------------------
+// stree_stats: block (chunk, row, kind); kind 0 = target rows, 1 = draft rows
+// (skipped for nodes without children: their draft rows are never used).
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(kSTThreads) void stree_stats_kernel(STreeArgs a) {
+  __shared__ double red[kSTWaves];
+  __shared__ float redf[kSTWaves];
+  const int ch = blockIdx.x, row = blockIdx.y, kind = blockIdx.z;
+  const int b = row / a.T, node = row % a.T;
+  if (kind == 1) {
+    // does the node have a child? one parent per thread, then a block OR
+    const int i = threadIdx.x;
+    const bool mine = i > node && i < a.T && a.parents[(size_t)b * a.T + i] == node;
+    if (!__syncthreads_or(mine)) return;       // uniform: the whole block leaves
+  }
+  const float* z = (kind == 0 ? a.target : a.draft) + (size_t)row * a.V;
+  const int begin = ch * kSTChunk, end = min(a.V, begin + kSTChunk);
+  constexpr int PER = kSTChunk / kSTThreads;
+  float x[PER];
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int v = begin + i * kSTThreads + threadIdx.x;
+    x[i] = v < end ? __builtin_nontemporal_load(z + v) : -__builtin_huge_valf();
+  }
+  float mx = x[0];
+#pragma unroll
+  for (int i = 1; i < PER; ++i) mx = fmaxf(mx, x[i]);
+  mx = block_max(mx, redf);
+  double s = 0.0;
+  // groups of four terms in float32 (at most 3 roundings), groups in float64
+#pragma unroll
+  for (int i = 0; i < PER; i += 4)
+    s += (double)((e_bulk(x[i], mx, a.k2f) + e_bulk(x[i + 1], mx, a.k2f)) +
+                  (e_bulk(x[i + 2], mx, a.k2f) + e_bulk(x[i + 3], mx, a.k2f)));
+  s = block_sum(s, red);
+  if (threadIdx.x == 0) {
+    const size_t o = ((size_t)kind * a.B * a.T + row) * a.nchunks + ch;
+    a.part_m[o] = mx;
+    a.part_s[o] = s;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// stree_walk.  CH > 0: V <= 512·CH, a visited node's rows are read once
+// (every load in flight, float4 loads when VEC) into registers (target) and
+// LDS (draft, token j0 + i of this thread at lq[i·512 + tid]: conflict-free).
+// CH = 0: any V, every pass streams the rows from memory.
+// ---------------------------------------------------------------------------
+template <int CH, bool VEC>
+__global__ __launch_bounds__(kSTThreads) void stree_walk_kernel(STreeArgs a) {
+  constexpr bool CACHED = CH > 0;
+  __shared__ int spar[64], stok[64], spath[65], shas[64];
+  __shared__ float sua[64];
+  __shared__ float nm_p[64], nm_q[64];       // every node's row maxima
+  __shared__ double ni_p[64], ni_q[64];      // and 1 / Σ e
+  __shared__ double ge_p[64], ge_q[64];      // e of node i's token in its parent's rows
+  __shared__ float lq[CACHED ? CH * kSTThreads : 1];
+  __shared__ double red[kSTWaves];
+  __shared__ int redi[kSTWaves];
+
+  const int b = blockIdx.x, tid = threadIdx.x, lane = tid & 63;
+  const int T = a.T, V = a.V;
+  const double k2 = a.k2;
+  if (tid < 64) shas[tid] = 0;
+  __syncthreads();
+  if (tid < T) {
+    const int pa = a.parents[(size_t)b * T + tid];
+    spar[tid] = pa;
+    stok[tid] = a.tokens[(size_t)b * T + tid];
+    sua[tid] = a.u_accept[(size_t)b * T + tid];
+    if (tid >= 1 && pa >= 0 && pa < tid) shas[pa] = 1;     // pa has a child
+  }
+  __syncthreads();
+  // Merge the chunk statistics of every row (target rows by threads 0..T-1,
+  // draft rows by 64..64+T-1); a draft row without statistics is never used.
+  if ((tid & 63) < T && tid < 128) {
+    const int kind = tid >> 6, node = tid & 63;
+    const size_t base = ((size_t)kind * a.B * T + (size_t)b * T + node) * a.nchunks;
+    const bool has_row = kind == 0 || shas[node] != 0;
+    float m = 0.f;
+    double inv = 1.0;
+    if (has_row) {
+      m = a.part_m[base];
+      for (int c = 1; c < a.nchunks; ++c) m = fmaxf(m, a.part_m[base + c]);
+      double s = 0.0;
+      for (int c = 0; c < a.nchunks; ++c)
+        s += a.part_s[base + c] * exp2_split(((double)a.part_m[base + c] - m) * k2);
+      inv = 1.0 / s;
+    }
+    if (kind == 0) { nm_p[node] = m; ni_p[node] = inv; }
+    else { nm_q[node] = m; ni_q[node] = inv; }
+  }
+  __syncthreads();
+  // e at every node's own token in its parent's target and draft rows.
+  if (tid < T) {
+    const int pa = spar[tid], x = stok[tid];
+    double ep = 0.0, eq = 0.0;
+    if (tid >= 1 && pa >= 0 && pa < tid && x >= 0 && x < V) {
+      const size_t r = ((size_t)b * T + pa) * V + x;
+      ep = e_of(a.target[r], nm_p[pa], k2);
+      eq = e_of(a.draft[r], nm_q[pa], k2);
+    }
+    ge_p[tid] = ep;
+    ge_q[tid] = eq;
+  }
+  __syncthreads();
+  // lane i of every wave stands for node i: the same masks in every wave
+  const int my_par = lane < T ? spar[lane] : -1;
+  const bool my_ok = lane >= 1 && lane < T && my_par >= 0 && my_par < lane;
+
+  // This thread's tokens (ascending, contiguous).
+  const int chs = CACHED ? CH : (V + kSTThreads - 1) / kSTThreads;
+  const int j0 = min(V, tid * chs), j1 = min(V, j0 + chs);
+
+  float rp[CACHED ? CH : 1];
+  auto q_at = [&](int i) -> float& { return lq[i * kSTThreads + tid]; };
+  int n = 0, depth = 0;
+  if (tid == 0) spath[0] = 0;
+  double c = 0.0, Z = 1.0;
+  const float* zt = nullptr;
+  const float* zq = nullptr;
+  float mp = 0.f, mq = 0.f;
+  double ip = 1.0, iq = 1.0;
+
+  // Reads the current node's rows as e values (cached path); the draft row
+  // only when `both`.
+  auto load_rows = [&](bool both) {
+    if constexpr (CACHED) {
+      if constexpr (VEC) {
+#pragma unroll
+        for (int i = 0; i < CH; i += 4) {
+          float4 x = make_float4(-__builtin_huge_valf(), -__builtin_huge_valf(),
+                                 -__builtin_huge_valf(), -__builtin_huge_valf());
+          float4 y = x;
+          if (j0 + i < V) {                       // V % 4 == 0 on this path
+            x = *(const float4*)(zt + j0 + i);
+            if (both) y = *(const float4*)(zq + j0 + i);
+          }
+          rp[i] = x.x; rp[i + 1] = x.y; rp[i + 2] = x.z; rp[i + 3] = x.w;
+          if (both) { q_at(i) = y.x; q_at(i + 1) = y.y; q_at(i + 2) = y.z; q_at(i + 3) = y.w; }
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < CH; ++i) {
+          const bool in = j0 + i < V;
+          rp[i] = in ? zt[j0 + i] : -__builtin_huge_valf();
+          if (both) q_at(i) = in ? zq[j0 + i] : -__builtin_huge_valf();
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < CH; ++i) {
+        rp[i] = e_bulk(rp[i], mp, a.k2f);
+        if (both) q_at(i) = e_bulk(q_at(i), mq, a.k2f);
+      }
+    }
+  };
+  // residual weight (p − c q)+ of token j0 + i (cached: float32 terms; q = p
+  // and c = 1 still cancel exactly) or v (streaming)
+  float ipf = 1.f, iqf = 1.f, cf = 0.f;
+  auto res_c = [&](int i) -> float {
+    return fmaxf(rp[i] * ipf - cf * (q_at(i) * iqf), 0.f);
+  };
+  auto res_s = [&](int v) -> double {
+    return fmax((double)e_bulk(zt[v], mp, a.k2f) * ip -
+                c * ((double)e_bulk(zq[v], mq, a.k2f) * iq), 0.0);
+  };
+
+  bool loaded = false;
+  while (true) {
+    const uint64_t kids = __ballot(my_ok && my_par == n);
+    zt = a.target + ((size_t)b * T + n) * V;
+    zq = a.draft + ((size_t)b * T + n) * V;
+    mp = nm_p[n]; ip = ni_p[n]; mq = nm_q[n]; iq = ni_q[n];
+    ipf = (float)ip; iqf = (float)iq;
+    loaded = false;
+    c = 0.0;
+    Z = 1.0;
+    int kept = -1;
+    for (uint64_t k = kids; k != 0; k &= k - 1) {
+      const int ch = __builtin_ctzll(k);
+      const int x = stok[ch];
+      double r = 0.0;
+      if (x >= 0 && x < V) {
+        const double px = ge_p[ch] * ip, qx = ge_q[ch] * iq;
+        const double w = fmax(px - c * qx, 0.0);
+        r = qx > 0.0 ? w / (Z * qx) : (w > 0.0 ? __builtin_huge_val() : 0.0);
+      }
+      if ((double)sua[ch] < r) {
+        kept = ch;
+        break;
+      }
+      // rejected: the residual moves on to (p − (c + Z) q)+
+      c += Z;
+      double s = 0.0;
+      if constexpr (CACHED) {
+        if (!loaded) { load_rows(true); loaded = true; }
+        launder(rp);
+        cf = (float)c;
+        // groups of four terms in float32, groups in float64
+#pragma unroll
+        for (int i = 0; i < CH; i += 4)
+          s += (double)((res_c(i) + res_c(i + 1)) + (res_c(i + 2) + res_c(i + 3)));
+      } else {
+        for (int v = tid; v < V; v += kSTThreads) s += res_s(v);
+      }
+      Z = block_sum(s, red);
+      if (!(Z > 0.0)) { c = 0.0; Z = 1.0; }    // an empty residual falls back to p
+    }
+    if (kept < 0) break;
+    ++depth;
+    if (tid == 0) spath[depth] = kept;
+    n = kept;
+  }
+
+  // Draw from w = (p − c q)+ (p itself when c = 0) with u_draw[b][n].
+  if constexpr (CACHED) {
+    if (!loaded) load_rows(c != 0.0);            // only c != 0 needs the draft row
+  }
+  cf = (float)c;
+  auto weight = [&](int i) -> double {         // token j0 + i
+    if constexpr (CACHED) return (double)(c == 0.0 ? rp[i] * ipf : res_c(i));
+    else return c == 0.0 ? (double)e_bulk(zt[j0 + i], mp, a.k2f) * ip : res_s(j0 + i);
+  };
+  double cs = 0.0;
+  if constexpr (CACHED) {
+    launder(rp);
+#pragma unroll
+    for (int i = 0; i < CH; ++i) cs += weight(i);     // tokens past V weigh 0
+  } else {
+    for (int i = 0; i < j1 - j0; ++i) cs += weight(i);
+  }
+  // exclusive scan of the chunk sums: within the wave, then the wave bases
+  double inc = cs;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const double y = __shfl_up(inc, o);
+    if (lane >= o) inc += y;
+  }
+  double ex = __shfl_up(inc, 1);
+  if (lane == 0) ex = 0.0;
+  __syncthreads();
+  if (lane == 63) red[tid >> 6] = inc;
+  __syncthreads();
+  double base = 0.0;
+  for (int w = 0; w < (tid >> 6); ++w) base += red[w];
+  double total = 0.0;
+#pragma unroll
+  for (int w = 0; w < kSTWaves; ++w) total += red[w];
+  ex += base;
+  const double thr = (double)a.u_draw[(size_t)b * T + n] * total;
+  // the weights are recomputed below rather than kept from the sum above
+  if constexpr (CACHED) launder(rp);
+  // this chunk's first token with positive weight whose running mass passes thr
+  int cand = V;
+  double run = ex;
+  if constexpr (CACHED) {
+#pragma unroll
+    for (int i = 0; i < CH; ++i) {
+      const double wi = weight(i);
+      run += wi;
+      if (cand == V && wi > 0.0 && run > thr) cand = j0 + i;
+    }
+  } else {
+    for (int i = 0; i < j1 - j0; ++i) {
+      const double wi = weight(i);
+      run += wi;
+      if (wi > 0.0 && run > thr) { cand = j0 + i; break; }
+    }
+  }
+  int y = block_min(cand, redi);
+  if (y >= V) y = V - 1;                      // nothing to draw (a zero total)
+
+  __syncthreads();
+  for (int i = tid; i < T; i += kSTThreads) {
+    const size_t o = (size_t)b * T + i;
+    a.path[o] = i <= depth ? spath[i] : -1;
+    a.out[o] = i < depth ? stok[spath[i + 1]] : (i == depth ? y : -1);
+  }
+  if (tid == 0) a.accept_len[b] = depth;
+}
+
+STreePlan plan_tree_sampled(int B, int T, int V) {
+  STreePlan p{};
+  p.nchunks = (V + kSTChunk - 1) / kSTChunk;
+  const size_t parts = (size_t)2 * B * T * p.nchunks;
+  p.s_bytes = align256(parts * sizeof(double));
+  p.m_bytes = align256(parts * sizeof(float));
+  p.total_bytes = p.s_bytes + p.m_bytes;
+  return p;
+}
+
+hipError_t launch_tree_sampled(const STreePlan& p, const float* target, const float* draft,
+                               const int32_t* tokens, const int32_t* parents,
+                               const float* u_accept, const float* u_draw, float temperature,
+                               int32_t* accept_len, int32_t* path, int32_t* out, int B, int T,
+                               int V, void* workspace, hipStream_t st) {
+  STreeArgs a;
+  a.target = target; a.draft = draft; a.tokens = tokens; a.parents = parents;
+  a.u_accept = u_accept; a.u_draw = u_draw;
+  a.accept_len = accept_len; a.path = path; a.out = out;
+  a.part_s = (double*)workspace;
+  a.part_m = (float*)((char*)workspace + p.s_bytes);
+  a.B = B; a.T = T; a.V = V; a.nchunks = p.nchunks;
+  a.k2 = 1.4426950408889634 / (double)temperature;
+  a.k2f = (float)a.k2;
+  stree_stats_kernel<<<dim3(p.nchunks, B * T, 2), kSTThreads, 0, st>>>(a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const bool vec = V % 4 == 0 && ((uintptr_t)target | (uintptr_t)draft) % 16 == 0;
+  const dim3 grid(B), block(kSTThreads);
+  if (V <= kSTThreads * 16) {
+    if (vec) stree_walk_kernel<16, true><<<grid, block, 0, st>>>(a);
+    else stree_walk_kernel<16, false><<<grid, block, 0, st>>>(a);
+  } else if (V <= kSTThreads * 32) {
+    if (vec) stree_walk_kernel<32, true><<<grid, block, 0, st>>>(a);
+    else stree_walk_kernel<32, false><<<grid, block, 0, st>>>(a);
+  } else if (V <= kSTThreads * 64) {
+    if (vec) stree_walk_kernel<64, true><<<grid, block, 0, st>>>(a);
+    else stree_walk_kernel<64, false><<<grid, block, 0, st>>>(a);
+  } else {
+    stree_walk_kernel<0, false><<<grid, block, 0, st>>>(a);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace sv

@@ -65,6 +65,11 @@ struct TreePlan {
   size_t part_bytes, total_bytes;
 };
 
+struct STreePlan {
+  int nchunks;     // 8192-logit statistics chunks per row
+  size_t s_bytes, m_bytes, total_bytes;
+};
+
 // A paged KV cache (see AttnArgs): position i of sequence b is row
 // i % page_size of page block_table[b][i / page_size].
 struct PagedKV {

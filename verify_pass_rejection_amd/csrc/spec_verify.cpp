@@ -22,6 +22,12 @@ TreePlan plan_tree(int B, int T, int V);
 hipError_t launch_tree(const TreePlan& p, const float* logits, const int32_t* tokens,
                        const int32_t* parents, int32_t* accept_len, int32_t* path,
                        int32_t* out, int B, int T, int V, void* workspace, hipStream_t st);
+STreePlan plan_tree_sampled(int B, int T, int V);
+hipError_t launch_tree_sampled(const STreePlan& p, const float* target, const float* draft,
+                               const int32_t* tokens, const int32_t* parents,
+                               const float* u_accept, const float* u_draw, float temperature,
+                               int32_t* accept_len, int32_t* path, int32_t* out, int B, int T,
+                               int V, void* workspace, hipStream_t st);
 hipError_t launch_commit(void* k, void* v, const int32_t* path, const int32_t* accept_len,
                          int32_t* new_len, int B, int T, int Hkv, int D, int ctx, int esize,
                          hipStream_t st);
@@ -178,6 +184,34 @@ spec_status spec_accept_tree(const float* target_logits, const int32_t* tokens,
   const hipError_t e = sv::launch_tree(p, target_logits, tokens, parents, accept_len, path,
                                        out_tokens, B, T, V, workspace,
                                        (hipStream_t)hip_stream);
+  return e == hipSuccess ? SPEC_OK : SPEC_ERR_HIP;
+}
+
+size_t spec_accept_tree_sampled_workspace(int B, int T, int V) {
+  if (check_tree(B, T, V) != SPEC_OK || B == 0 || T == 0) return 0;
+  return sv::plan_tree_sampled(B, T, V).total_bytes;
+}
+
+spec_status spec_accept_tree_sampled(const float* target_logits, const float* draft_logits,
+                                     const int32_t* tokens, const int32_t* parents,
+                                     const float* u_accept, const float* u_draw,
+                                     float temperature, int32_t* accept_len, int32_t* path,
+                                     int32_t* out_tokens, int B, int T, int V,
+                                     void* workspace, size_t workspace_bytes,
+                                     void* hip_stream) {
+  const spec_status c = check_tree(B, T, V);
+  if (c != SPEC_OK) return c;
+  if (!(temperature > 0.f) || !isfinite(temperature)) return SPEC_ERR_SHAPE;
+  if (B == 0 || T == 0) return SPEC_OK;
+  if (!target_logits || !draft_logits || !tokens || !parents || !u_accept || !u_draw ||
+      !accept_len || !path || !out_tokens || !workspace)
+    return SPEC_ERR_NULL;
+  const sv::STreePlan p = sv::plan_tree_sampled(B, T, V);
+  if (workspace_bytes < p.total_bytes) return SPEC_ERR_WORKSPACE;
+  const hipError_t e = sv::launch_tree_sampled(p, target_logits, draft_logits, tokens, parents,
+                                               u_accept, u_draw, temperature, accept_len, path,
+                                               out_tokens, B, T, V, workspace,
+                                               (hipStream_t)hip_stream);
   return e == hipSuccess ? SPEC_OK : SPEC_ERR_HIP;
 }
 

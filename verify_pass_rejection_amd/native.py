@@ -38,6 +38,9 @@ _SIGNATURES = {
     "spec_accept_tree_workspace": (_c.c_size_t, [_c.c_int] * 3),
     "spec_accept_tree": (_c.c_int, [_c.c_void_p] * 6 + [_c.c_int] * 3
                          + [_c.c_void_p, _c.c_size_t, _c.c_void_p]),
+    "spec_accept_tree_sampled_workspace": (_c.c_size_t, [_c.c_int] * 3),
+    "spec_accept_tree_sampled": (_c.c_int, [_c.c_void_p] * 6 + [_c.c_float] + [_c.c_void_p] * 3
+                                 + [_c.c_int] * 3 + [_c.c_void_p, _c.c_size_t, _c.c_void_p]),
     "spec_commit_kv": (_c.c_int, [_c.c_void_p] * 5 + [_c.c_int] * 5 + [_c.c_int, _c.c_void_p]),
 }
 
@@ -256,6 +259,37 @@ def spec_accept_tree(target_logits, tokens, parents, accept_len=None, path=None,
                                  _ptr(accept_len), _ptr(path), _ptr(out_tokens), B, T, V,
                                  _ptr(ws), ws.numel() * ws.element_size(), _stream(stream))
     _raise(st, "spec_accept_tree")
+    return accept_len, path, out_tokens
+
+
+def spec_accept_tree_sampled_workspace(B, T, V) -> int:
+    return int(load().spec_accept_tree_sampled_workspace(B, T, V))
+
+
+def spec_accept_tree_sampled(target_logits, draft_logits, tokens, parents, u_accept, u_draw,
+                             temperature=1.0, accept_len=None, path=None, out_tokens=None,
+                             workspace=None, stream=None):
+    """Sampled tree acceptance; returns (accept_len [B], path [B,T], out_tokens [B,T])."""
+    B, T, V = target_logits.shape
+    dev = target_logits.device
+    _check(target_logits, "target_logits", (B, T, V), torch.float32, dev)
+    _check(draft_logits, "draft_logits", (B, T, V), torch.float32, dev)
+    _check(tokens, "tokens", (B, T), torch.int32, dev)
+    _check(parents, "parents", (B, T), torch.int32, dev)
+    _check(u_accept, "u_accept", (B, T), torch.float32, dev)
+    _check(u_draw, "u_draw", (B, T), torch.float32, dev)
+    if accept_len is None:
+        accept_len = torch.empty(B, dtype=torch.int32, device=dev)
+    if path is None:
+        path = torch.empty((B, T), dtype=torch.int32, device=dev)
+    if out_tokens is None:
+        out_tokens = torch.empty((B, T), dtype=torch.int32, device=dev)
+    ws = _workspace(spec_accept_tree_sampled_workspace(B, T, V), dev, workspace)
+    st = load().spec_accept_tree_sampled(
+        _ptr(target_logits), _ptr(draft_logits), _ptr(tokens), _ptr(parents), _ptr(u_accept),
+        _ptr(u_draw), float(temperature), _ptr(accept_len), _ptr(path), _ptr(out_tokens),
+        B, T, V, _ptr(ws), ws.numel() * ws.element_size(), _stream(stream))
+    _raise(st, "spec_accept_tree_sampled")
     return accept_len, path, out_tokens
 
 
