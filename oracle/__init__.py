@@ -27,6 +27,8 @@ Modules:
 * :mod:`oracle.commit`    — the KV commit of the accepted path (a gather).
 * :mod:`oracle.paged`     — verify attention over a paged KV cache (a gather
   of each sequence's pages, then :mod:`oracle.attention`).
+* :mod:`oracle.ngram`     — n-gram (prompt-lookup) draft proposal, a search
+  from the longest n-gram and the latest position down.
 
 Parity status: every function here is pinned by ``-m "not gpu"`` tests against
 something other than itself (a library routine, a closed form, brute force,

@@ -27,7 +27,8 @@ import torch
 # Named substreams: a per-input offset added to the workload seed.
 _STREAMS = {"q": 1, "k": 2, "v": 3, "target": 4, "draft_noise": 5,
             "draft_gumbel": 6, "u_accept": 7, "u_draw": 8, "tree": 9,
-            "tree_tokens": 10, "ctx_lens": 11, "pages": 12, "stree_gumbel": 13}
+            "tree_tokens": 10, "ctx_lens": 11, "pages": 12, "stree_gumbel": 13,
+            "ngram": 14}
 
 #: Spike written into a parent's logit row at the planted child's token, in
 #: units of the logit standard deviation (8σ is never reached by N(0, σ²)
@@ -271,6 +272,35 @@ def make_sampled_tree_inputs(w: Workload, device="cpu", draft_noise_sd: float = 
                 tokens=tokens.to(torch.int32), parents=par.to(torch.int32),
                 u_accept=uniforms((B, T), _gen(w, "u_accept", device), device),
                 u_draw=uniforms((B, T), _gen(w, "u_draw", device), device))
+
+
+def make_ngram_inputs(w: Workload, device="cpu", copy_prob: float = 0.5,
+                      span=(16, 256)):
+    """Token histories [B, ctx] int32 for n-gram drafting, and lengths [B].
+
+    A history is built span by span (span lengths uniform in ``span``): the
+    first span is fresh, each later one is, with probability copy_prob, a
+    copy of an earlier stretch of the same history, else fresh tokens
+    uniform over the vocabulary — a repetitive load with prompt-lookup hits.
+    Lengths are uniform in [ctx/2, ctx], sequence 0 at ctx.
+    """
+    g = torch.Generator().manual_seed(w.seed * 1000 + _STREAMS["ngram"])
+    B, L, V = w.B, w.ctx, w.V
+    ctx = torch.empty((B, L), dtype=torch.int64)
+    for b in range(B):
+        pos = 0
+        while pos < L:
+            n = min(L - pos, int(torch.randint(span[0], span[1] + 1, (1,), generator=g)))
+            if pos >= span[0] and float(torch.rand((1,), generator=g)) < copy_prob:
+                src = int(torch.randint(0, pos - min(n, pos) + 1, (1,), generator=g))
+                n = min(n, pos - src)
+                ctx[b, pos:pos + n] = ctx[b, src:src + n]
+            else:
+                ctx[b, pos:pos + n] = torch.randint(0, V, (n,), generator=g)
+            pos += n
+    lens = torch.randint(max(1, L // 2), L + 1, (B,), generator=g)
+    lens[0] = L
+    return ctx.to(torch.int32).to(device), lens.to(torch.int32).to(device)
 
 
 def ragged_ctx_lens(w: Workload, device="cpu") -> torch.Tensor:
