@@ -12,8 +12,9 @@ verification overhead α = (T(N) − T(0)) / (N·T(0)) at N = 4 and 8 on the sam
 shape, a roofline entry for the attention kernel and the CPU oracle's rate on a
 bounded sample of the same workload.  Beside the line's own figures: the
 attention call over a paged copy of the same cache (pages of 16 positions),
-and for trees the KV commit of the accepted path and the sampled (non-greedy)
-acceptance of the same tree shape.
+for trees the KV commit of the accepted path and the sampled (non-greedy)
+acceptance of the same tree shape, and for chains the n-gram draft proposal
+over histories of the same batch and length.
 """
 from __future__ import annotations
 
@@ -259,6 +260,41 @@ def time_sampled_tree(w, dev, steps: int, flush=None):
                     "statistics pass"}
 
 
+def time_ngram(w, dev, steps: int, flush=None, n_min: int = 1, n_max: int = 4):
+    """spec_ngram_propose for the workload's batch: histories of ctx tokens
+    (the seeded repetitive recipe, lengths in [ctx/2, ctx]), N = the
+    workload's draft count; per-call events.  Bytes: every history token
+    once."""
+    import torch
+    from verify_pass_rejection_amd import inputs as I
+    from verify_pass_rejection_amd import native as nat
+    ctx, lens = I.make_ngram_inputs(w, dev)
+    num, drafts = nat.spec_ngram_propose(ctx, w.N, n_min, n_max, context_lens=lens)
+    ws = torch.empty(max(1, nat.spec_ngram_propose_workspace(w.B, w.ctx)), dtype=torch.uint8,
+                     device=dev)
+    run = lambda: nat.spec_ngram_propose(ctx, w.N, n_min, n_max, context_lens=lens,  # noqa: E731
+                                         num_drafts=num, drafts=drafts, workspace=ws)
+    for _ in range(3):
+        run()
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
+    for i in range(steps):
+        if flush is not None:
+            flush.zero_()
+        ev[i][0].record()
+        run()
+        ev[i][1].record()
+    torch.cuda.synchronize()
+    ts = [a.elapsed_time(b) * 1e3 for a, b in ev]
+    us = pct(ts, 0.5)
+    nbytes = int(lens.long().sum()) * 4
+    return {"us": round(us, 2), "us_p10_p50_p90": [round(pct(ts, q), 2) for q in (0.1, 0.5, 0.9)],
+            "bytes": nbytes, "GBps": round(nbytes / (us * 1e-6) / 1e9, 1),
+            "n_min": n_min, "n_max": n_max,
+            "mean_drafts": round(float(num.float().mean()), 3),
+            "note": "latency-bound: a few MB per call"}
+
+
 def cpu_baseline(w, step, budget_s: float = 30.0):
     """The fp64 oracle on a bounded sample: sequence 0 of the same batch
     (attention for all its heads and positions, then its acceptance)."""
@@ -401,6 +437,8 @@ def main():
 
     paged = None if args.no_paged else time_paged(step, args.steps, flush)
 
+    ngram = time_ngram(w, dev, args.steps, flush) if w.kind == "chain" and w.N > 0 else None
+
     commit = sampled = None
     if w.kind == "tree":
         commit = time_commit(step, args.steps)
@@ -453,6 +491,8 @@ def main():
         line["kv_commit"] = commit
     if sampled is not None:
         line["sampled_tree_acceptance"] = sampled
+    if ngram is not None:
+        line["ngram_proposal"] = ngram
     print(json.dumps(line), flush=True)
 
 

@@ -260,6 +260,35 @@ spec_status spec_accept_tree_sampled(const float* target_logits, const float* dr
                                      void* hip_stream);
 
 /* ---------------------------------------------------------------------------
+ * n-gram (prompt-lookup) draft proposal ("LLM Primer VI", section "Pourquoi
+ * ce chapitre existe": n-gram and suffix drafting among the draft algorithms;
+ * §9.3: the largest speedups on highly repetitive loads; "Parallel Decoding"
+ * glossary, "Parallel decoding en production": prompt lookup).
+ *
+ * For sequence b with history c[0..Lb-1] (Lb = context_lens[b], clamped to
+ * [0, L]): for n = n_max down to n_min, the last n tokens are searched among
+ * the earlier n-grams c[e-n+1..e], e <= Lb-2; the first n with an occurrence
+ * wins and its most recent occurrence (largest e) is taken.  The drafts are
+ * c[e+1 .. min(e+N, Lb-1)]; without an occurrence there is none.
+ *
+ *   context       [B, L] int32 token ids (positions >= context_lens[b] ignored)
+ *   context_lens  [B] int32, or NULL (every history has L tokens)
+ *   num_drafts    [B] int32 out: number of drafts (0..N)
+ *   drafts        [B, N] int32 out: the drafts, then -1
+ *
+ * Limits: 0 <= N <= SPEC_MAX_T - 1, 1 <= n_min <= n_max <= SPEC_NGRAM_MAX.
+ * Workspace: spec_ngram_propose_workspace(B, L).
+ * ------------------------------------------------------------------------- */
+#define SPEC_NGRAM_MAX 16
+
+size_t spec_ngram_propose_workspace(int B, int L);
+
+spec_status spec_ngram_propose(const int32_t* context, const int32_t* context_lens,
+                               int32_t* num_drafts, int32_t* drafts,
+                               int B, int L, int N, int n_min, int n_max,
+                               void* workspace, size_t workspace_bytes, void* hip_stream);
+
+/* ---------------------------------------------------------------------------
  * KV commit after acceptance (Primer §9.1: at the first divergence the engine
  * commits to the target's choice and drops the rest; glossary "Limites du
  * parallel decoding": tree attention keeps every branch's keys and values in

@@ -25,7 +25,7 @@ def declared_functions():
 def test_library_loads_and_exports_every_declared_symbol():
     lib = nat.load()
     decl = declared_functions()
-    assert len(decl) == 12
+    assert len(decl) == 14
     for name in decl:
         assert hasattr(lib, name), name
     assert sorted(nat.exported_symbols()) == decl
@@ -216,6 +216,34 @@ def test_sampled_tree_validation():
     f = nat.spec_accept_tree_sampled_workspace
     assert f(8, 64, 32000) >= 2 * 8 * 64 * 4 * 12 and f(8, 64, 32000) % 256 == 0
     assert f(0, 64, 32000) == 0 and f(8, 65, 32000) == 0
+
+
+def ngram(**kw):
+    a = dict(c=FAKE, lens=None, num=FAKE, d=FAKE, B=4, L=1000, N=8, n_min=1, n_max=4, ws=FAKE,
+             ws_bytes=1 << 40, stream=None)
+    a.update(kw)
+    return nat.load().spec_ngram_propose(a["c"], a["lens"], a["num"], a["d"], a["B"], a["L"],
+                                         a["N"], a["n_min"], a["n_max"], a["ws"],
+                                         a["ws_bytes"], a["stream"])
+
+
+def test_ngram_validation():
+    assert ngram(c=None) == NULL
+    assert ngram(num=None) == NULL
+    assert ngram(d=None) == NULL
+    assert ngram(ws=None) == NULL
+    assert ngram(B=-1) == SHAPE
+    assert ngram(L=-1) == SHAPE
+    assert ngram(N=-1) == SHAPE
+    assert ngram(n_min=0) == SHAPE
+    assert ngram(n_min=3, n_max=2) == SHAPE
+    assert ngram(N=64) == UNSUP
+    assert ngram(n_max=17) == UNSUP
+    assert ngram(ws_bytes=8) == WS
+    assert ngram(B=0, c=None) == OK
+    f = nat.spec_ngram_propose_workspace
+    assert f(64, 32768) >= 64 * 8 * 8 and f(64, 32768) % 256 == 0
+    assert f(0, 100) == 0
 
 
 def test_commit_validation():

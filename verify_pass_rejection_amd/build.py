@@ -16,7 +16,7 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libspecverify.so")
 SOURCES = ["attention.hip", "accept_chain.hip", "accept_tree.hip", "accept_tree_sampled.hip",
-           "commit.hip", "spec_verify.cpp"]
+           "commit.hip", "ngram.hip", "spec_verify.cpp"]
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -70,6 +70,11 @@ struct STreePlan {
   size_t s_bytes, m_bytes, total_bytes;
 };
 
+struct NgramPlan {
+  int tiles;       // 4096-position tiles per sequence
+  size_t total_bytes;
+};
+
 // A paged KV cache (see AttnArgs): position i of sequence b is row
 // i % page_size of page block_table[b][i / page_size].
 struct PagedKV {

@@ -28,6 +28,10 @@ hipError_t launch_tree_sampled(const STreePlan& p, const float* target, const fl
                                const float* u_accept, const float* u_draw, float temperature,
                                int32_t* accept_len, int32_t* path, int32_t* out, int B, int T,
                                int V, void* workspace, hipStream_t st);
+NgramPlan plan_ngram(int B, int L);
+hipError_t launch_ngram(const NgramPlan& p, const int32_t* ctx, const int32_t* lens,
+                        int32_t* num, int32_t* drafts, int B, int L, int N, int n_min,
+                        int n_max, void* workspace, hipStream_t st);
 hipError_t launch_commit(void* k, void* v, const int32_t* path, const int32_t* accept_len,
                          int32_t* new_len, int B, int T, int Hkv, int D, int ctx, int esize,
                          hipStream_t st);
@@ -48,6 +52,12 @@ spec_status check_attention(int B, int T, int Hq, int Hkv, int D, int ctx, spec_
 spec_status check_chain(int B, int N, int V) {
   if (B < 0 || N < 0 || V < 1) return SPEC_ERR_SHAPE;
   if (V > SPEC_MAX_V || N > SPEC_MAX_T - 1) return SPEC_ERR_UNSUPPORTED;
+  return SPEC_OK;
+}
+
+spec_status check_ngram(int B, int L, int N, int n_min, int n_max) {
+  if (B < 0 || L < 0 || N < 0 || n_min < 1 || n_max < n_min) return SPEC_ERR_SHAPE;
+  if (N > SPEC_MAX_T - 1 || n_max > SPEC_NGRAM_MAX) return SPEC_ERR_UNSUPPORTED;
   return SPEC_OK;
 }
 
@@ -212,6 +222,27 @@ spec_status spec_accept_tree_sampled(const float* target_logits, const float* dr
                                                u_accept, u_draw, temperature, accept_len, path,
                                                out_tokens, B, T, V, workspace,
                                                (hipStream_t)hip_stream);
+  return e == hipSuccess ? SPEC_OK : SPEC_ERR_HIP;
+}
+
+size_t spec_ngram_propose_workspace(int B, int L) {
+  if (B < 1 || L < 0) return 0;
+  return sv::plan_ngram(B, L).total_bytes;
+}
+
+spec_status spec_ngram_propose(const int32_t* context, const int32_t* context_lens,
+                               int32_t* num_drafts, int32_t* drafts, int B, int L, int N,
+                               int n_min, int n_max, void* workspace, size_t workspace_bytes,
+                               void* hip_stream) {
+  const spec_status c = check_ngram(B, L, N, n_min, n_max);
+  if (c != SPEC_OK) return c;
+  if (B == 0) return SPEC_OK;
+  if (!num_drafts || !workspace || (L > 0 && !context) || (N > 0 && !drafts))
+    return SPEC_ERR_NULL;
+  const sv::NgramPlan p = sv::plan_ngram(B, L);
+  if (workspace_bytes < p.total_bytes) return SPEC_ERR_WORKSPACE;
+  const hipError_t e = sv::launch_ngram(p, context, context_lens, num_drafts, drafts, B, L, N,
+                                        n_min, n_max, workspace, (hipStream_t)hip_stream);
   return e == hipSuccess ? SPEC_OK : SPEC_ERR_HIP;
 }
 

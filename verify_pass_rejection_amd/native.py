@@ -41,6 +41,9 @@ _SIGNATURES = {
     "spec_accept_tree_sampled_workspace": (_c.c_size_t, [_c.c_int] * 3),
     "spec_accept_tree_sampled": (_c.c_int, [_c.c_void_p] * 6 + [_c.c_float] + [_c.c_void_p] * 3
                                  + [_c.c_int] * 3 + [_c.c_void_p, _c.c_size_t, _c.c_void_p]),
+    "spec_ngram_propose_workspace": (_c.c_size_t, [_c.c_int] * 2),
+    "spec_ngram_propose": (_c.c_int, [_c.c_void_p] * 4 + [_c.c_int] * 5
+                           + [_c.c_void_p, _c.c_size_t, _c.c_void_p]),
     "spec_commit_kv": (_c.c_int, [_c.c_void_p] * 5 + [_c.c_int] * 5 + [_c.c_int, _c.c_void_p]),
 }
 
@@ -291,6 +294,31 @@ def spec_accept_tree_sampled(target_logits, draft_logits, tokens, parents, u_acc
         B, T, V, _ptr(ws), ws.numel() * ws.element_size(), _stream(stream))
     _raise(st, "spec_accept_tree_sampled")
     return accept_len, path, out_tokens
+
+
+def spec_ngram_propose_workspace(B, L) -> int:
+    return int(load().spec_ngram_propose_workspace(B, L))
+
+
+def spec_ngram_propose(context, N, n_min=1, n_max=4, context_lens=None, num_drafts=None,
+                       drafts=None, workspace=None, stream=None):
+    """n-gram draft proposal; returns (num_drafts [B], drafts [B, N]) int32."""
+    B, L = context.shape
+    dev = context.device
+    _check(context, "context", (B, L), torch.int32, dev)
+    if context_lens is not None:
+        _check(context_lens, "context_lens", (B,), torch.int32, dev)
+    if num_drafts is None:
+        num_drafts = torch.empty(B, dtype=torch.int32, device=dev)
+    if drafts is None:
+        drafts = torch.empty((B, N), dtype=torch.int32, device=dev)
+    _check(drafts, "drafts", (B, N), torch.int32, dev)
+    ws = _workspace(spec_ngram_propose_workspace(B, L), dev, workspace)
+    st = load().spec_ngram_propose(_ptr(context), _ptr(context_lens), _ptr(num_drafts),
+                                   _ptr(drafts), B, L, N, n_min, n_max, _ptr(ws),
+                                   ws.numel() * ws.element_size(), _stream(stream))
+    _raise(st, "spec_ngram_propose")
+    return num_drafts, drafts
 
 
 def spec_commit_kv(k, v, ctx, accept_len, path=None, new_len=None, stream=None):
