@@ -52,6 +52,7 @@ def compare(d, temperature=1.0, label=""):
     ("eagle2_tree", dict(B=4, V=4000)),
     ("medusa70b_tree", dict(B=6, V=3001)),          # V not a multiple of 4
     ("eagle2_tree", dict(B=64, V=777)),              # many sequences, chunks of one token
+    ("eagle2_tree", dict(B=3, V=40000)),             # V > 32768: rows streamed per pass
     ("eagle2_tree", dict()),                         # full reference size
     ("medusa70b_tree", dict()),                      # full reference size
 ])
