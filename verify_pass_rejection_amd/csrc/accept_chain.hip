@@ -10,7 +10,7 @@
 // Three kernels (kernel boundaries order every step; no in-kernel signalling):
 //  chain_stats  — one pass over every logit row (all B*(2N+1) rows), per chunk
 //                 the row maximum and sum of 2^((z - max) log2(e)/tau);
-//  chain_chunks — grid (vocabulary chunk, sequence): every block first takes
+//  chain_chunks — grid (group of draw chunks, sequence): every block first takes
 //                 the sequence's decision (merges the chunk statistics into
 //                 the row normalisers, runs the N ratio tests with two gathers
 //                 a row, takes the first rejection k), then sums the weights
@@ -60,10 +60,11 @@ constexpr int kStatsChunk = SV_STATS_CHUNK;   // logits per stats block
 constexpr int kDrawThreads = 1024;
 constexpr int kDrawPer = SV_DRAW_PER; // weights per thread per draw chunk
 constexpr int kDrawChunk = kDrawThreads * kDrawPer;
-#ifndef SV_DRAW_CPB
-#define SV_DRAW_CPB 3
-#endif
-constexpr int kDrawCpb = SV_DRAW_CPB;  // draw chunks summed per chain_chunks block
+// Draw chunks summed per chain_chunks block: three on large batches (fewer,
+// fuller blocks), one when a chunk per block still fits one wave of resident
+// blocks (small batches are latency-bound: more blocks, shorter each).
+constexpr int kDrawCpbLarge = 3;
+constexpr int kDrawResident = 512;    // 1024-thread blocks resident on 256 CUs
 
 __device__ __forceinline__ const float* chain_row(const ChainArgs& a, int b, int rho) {
   return rho <= a.N ? a.target + ((size_t)b * (a.N + 1) + rho) * a.V
@@ -150,48 +151,73 @@ __global__ __launch_bounds__(kStatsThreads) void chain_stats_kernel(ChainArgs a)
   }
 }
 
-// Weights of the drawn row: residual (p - q)+ or p alone.
+// The drawn row: weights (p - q)+ (RESID) or p alone.
 struct DrawRow {
   const float* zp;
-  const float* zq;   // nullptr: weights are p
+  const float* zq;   // read only when RESID
   float mp, lp;      // row max and log2 of the sum for p
   float mq, lq;
   float c;
-  __device__ __forceinline__ float w(float xp, float xq) const {
-    const float p = fast_exp2((xp - mp) * c - lp);
-    if (zq == nullptr) return p;
-    const float q = fast_exp2((xq - mq) * c - lq);
-    return fmaxf(p - q, 0.f);
-  }
 };
 
-// Loads the kDrawPer weights of this thread in draw chunk `chunk`.
-template <int VEC>
-__device__ __forceinline__ void draw_weights(const DrawRow& r, int V, int chunk, float* w) {
+template <bool RESID>
+__device__ __forceinline__ float draw_w(const DrawRow& r, float xp, float xq) {
+  const float p = fast_exp2((xp - r.mp) * r.c - r.lp);
+  if constexpr (!RESID) return p;
+  const float q = fast_exp2((xq - r.mq) * r.c - r.lq);
+  return fmaxf(p - q, 0.f);
+}
+
+// Logits of this thread's kDrawPer tokens in draw chunk `chunk`.  Indices are
+// clamped into the row so that every load is issued without a branch (a
+// branch around each load makes the compiler wait for each one in turn); the
+// weights of tokens past the row are zeroed by draw_weights_from.
+template <int VEC, bool RESID>
+__device__ __forceinline__ void draw_load(const DrawRow& r, int V, int chunk, float* xp,
+                                          float* xq) {
   const int j0 = chunk * kDrawChunk + threadIdx.x * kDrawPer;
-  float xp[kDrawPer], xq[kDrawPer];
   if constexpr (VEC == 4) {
     static_assert(kDrawPer % 4 == 0, "whole float4 per thread");
 #pragma unroll
     for (int i = 0; i < kDrawPer; i += 4) {
-      float4 p4 = {kNegInf, kNegInf, kNegInf, kNegInf}, q4 = p4;
-      if (j0 + i < V) {                 // V % 4 == 0 on this path: all four in range
-        p4 = load_draw4(r.zp + j0 + i);
-        if (r.zq) q4 = load_draw4(r.zq + j0 + i);
-      }
+      const int j = min(j0 + i, V - 4);     // V % 4 == 0 on this path
+      const float4 p4 = load_draw4(r.zp + j);
       xp[i] = p4.x; xp[i + 1] = p4.y; xp[i + 2] = p4.z; xp[i + 3] = p4.w;
-      xq[i] = q4.x; xq[i + 1] = q4.y; xq[i + 2] = q4.z; xq[i + 3] = q4.w;
+      if constexpr (RESID) {
+        const float4 q4 = load_draw4(r.zq + j);
+        xq[i] = q4.x; xq[i + 1] = q4.y; xq[i + 2] = q4.z; xq[i + 3] = q4.w;
+      }
     }
   } else {
 #pragma unroll
     for (int e = 0; e < kDrawPer; ++e) {
-      const int j = j0 + e;
-      xp[e] = j < V ? r.zp[j] : kNegInf;
-      xq[e] = (j < V && r.zq) ? r.zq[j] : kNegInf;
+      const int j = min(j0 + e, V - 1);
+      xp[e] = r.zp[j];
+      if constexpr (RESID) xq[e] = r.zq[j];
     }
   }
+}
+
+template <bool RESID>
+__device__ __forceinline__ void draw_weights_from(const DrawRow& r, int V, int chunk,
+                                                  const float* xp, const float* xq, float* w) {
+  const int j0 = chunk * kDrawChunk + threadIdx.x * kDrawPer;
 #pragma unroll
-  for (int e = 0; e < kDrawPer; ++e) w[e] = (j0 + e < V) ? r.w(xp[e], xq[e]) : 0.f;
+  for (int e = 0; e < kDrawPer; ++e) w[e] = (j0 + e < V) ? draw_w<RESID>(r, xp[e], xq[e]) : 0.f;
+}
+
+// The kDrawPer weights of this thread in draw chunk `chunk` (RESID or not is
+// a block-uniform choice).
+template <int VEC, bool RESID>
+__device__ __forceinline__ void draw_weights(const DrawRow& r, int V, int chunk, float* w) {
+  float xp[kDrawPer], xq[kDrawPer];
+  draw_load<VEC, RESID>(r, V, chunk, xp, xq);
+  draw_weights_from<RESID>(r, V, chunk, xp, xq, w);
+}
+template <int VEC>
+__device__ __forceinline__ void draw_weights(const DrawRow& r, int V, int chunk, float* w) {
+  if (r.zq != nullptr) draw_weights<VEC, true>(r, V, chunk, w);
+  else draw_weights<VEC, false>(r, V, chunk, w);
 }
 
 // Running sums inside one draw chunk, in a fixed order: the thread's own
@@ -300,16 +326,35 @@ __device__ __forceinline__ void draw_rows(const ChainArgs& a, int b, int& k, Dra
   }
 }
 
+// Chunk sums of draw chunks [c0, c0 + CPB) of the drawn row: every load
+// first, then one scan per chunk (chunks past the row are not written).
+template <int VEC, int CPB, bool RESID>
+__device__ __forceinline__ void chunk_sums(const ChainArgs& a, const DrawRow& r, int b, int c0,
+                                           float* wave_tot, float* wave_off) {
+  float xp[CPB][kDrawPer], xq[CPB][kDrawPer];
+#pragma unroll
+  for (int cc = 0; cc < CPB; ++cc) draw_load<VEC, RESID>(r, a.V, c0 + cc, xp[cc], xq[cc]);
+#pragma unroll
+  for (int cc = 0; cc < CPB; ++cc) {
+    const int ch = c0 + cc;
+    if (ch >= a.dchunks) break;
+    float w[kDrawPer], pre[kDrawPer];
+    draw_weights_from<RESID>(r, a.V, ch, xp[cc], xq[cc], w);
+    chunk_scan(w, pre, wave_tot, wave_off);
+    if (threadIdx.x == kDrawThreads - 1) a.csum[(size_t)b * 2 * a.dchunks + ch] = pre[kDrawPer - 1];
+  }
+}
+
 // Every block of a sequence takes the decision itself (the statistics are
 // small), so that no launch sits between the statistics and the draw, and
-// then sums kDrawCpb chunks of the drawn row; block 0 records the decision
-// for chain_select.
-template <int VEC>
+// then sums CPB chunks of the drawn row; block 0 records the decision for
+// chain_select.
+template <int VEC, int CPB>
 __global__ __launch_bounds__(kDrawThreads) void chain_chunks_kernel(ChainArgs a) {
   __shared__ float wave_tot[kDrawThreads / kWave], wave_off[kDrawThreads / kWave];
   __shared__ float row_m[128], row_l[128];
   __shared__ int keep[64], s_k;
-  const int c = blockIdx.x, b = blockIdx.y, nch = a.dchunks, N = a.N;
+  const int c = blockIdx.x, b = blockIdx.y, N = a.N;
   const int k = chain_decision<kDrawThreads>(a, b, row_m, row_l, keep, &s_k);
   DrawRow dr;
   dr.zp = a.target + ((size_t)b * (N + 1) + k) * a.V;
@@ -327,19 +372,8 @@ __global__ __launch_bounds__(kDrawThreads) void chain_chunks_kernel(ChainArgs a)
     a.decision[b] = make_float4(__int_as_float(k), row_m[k], row_l[k], 0.f);
     a.decision_q[b] = make_float4(dr.mq, dr.lq, 0.f, 0.f);
   }
-  // This block's kDrawCpb chunks: every load first, then one scan per chunk
-  // (chunks past the row have zero weights and are not written).
-  float w[kDrawCpb][kDrawPer];
-#pragma unroll
-  for (int cc = 0; cc < kDrawCpb; ++cc) draw_weights<VEC>(dr, a.V, c * kDrawCpb + cc, w[cc]);
-#pragma unroll
-  for (int cc = 0; cc < kDrawCpb; ++cc) {
-    const int ch = c * kDrawCpb + cc;
-    if (ch >= nch) break;
-    float pre[kDrawPer];
-    chunk_scan(w[cc], pre, wave_tot, wave_off);
-    if (threadIdx.x == kDrawThreads - 1) a.csum[(size_t)b * 2 * nch + ch] = pre[kDrawPer - 1];
-  }
+  if (k < N) chunk_sums<VEC, CPB, true>(a, dr, b, c * CPB, wave_tot, wave_off);
+  else chunk_sums<VEC, CPB, false>(a, dr, b, c * CPB, wave_tot, wave_off);
 }
 
 template <int VEC>
@@ -460,6 +494,7 @@ ChainPlan plan_chain(int B, int N, int V) {
   p.chunk = kStatsChunk;
   p.nchunks = (V + kStatsChunk - 1) / kStatsChunk;
   p.dchunks = (V + kDrawChunk - 1) / kDrawChunk;
+  p.cpb = (size_t)B * p.dchunks <= kDrawResident ? 1 : kDrawCpbLarge;
   p.stats_bytes = align256((size_t)B * p.rows_per_seq * p.nchunks * sizeof(float2));
   p.csum_bytes = align256((size_t)B * 2 * p.dchunks * sizeof(float));
   p.decision_bytes = align256((size_t)B * 2 * sizeof(float4));
@@ -487,9 +522,14 @@ hipError_t launch_chain(const ChainPlan& p, const float* target, const float* dr
   else chain_stats_kernel<1><<<g1, kStatsThreads, 0, st>>>(a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const dim3 g2((p.dchunks + kDrawCpb - 1) / kDrawCpb, B);
-  if (vec4) chain_chunks_kernel<4><<<g2, kDrawThreads, 0, st>>>(a);
-  else chain_chunks_kernel<1><<<g2, kDrawThreads, 0, st>>>(a);
+  const dim3 g2((p.dchunks + p.cpb - 1) / p.cpb, B);
+  if (p.cpb == 1) {
+    if (vec4) chain_chunks_kernel<4, 1><<<g2, kDrawThreads, 0, st>>>(a);
+    else chain_chunks_kernel<1, 1><<<g2, kDrawThreads, 0, st>>>(a);
+  } else {
+    if (vec4) chain_chunks_kernel<4, kDrawCpbLarge><<<g2, kDrawThreads, 0, st>>>(a);
+    else chain_chunks_kernel<1, kDrawCpbLarge><<<g2, kDrawThreads, 0, st>>>(a);
+  }
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (vec4) chain_select_kernel<4><<<B, kDrawThreads, 0, st>>>(a);
