@@ -60,10 +60,12 @@ constexpr int kStatsChunk = SV_STATS_CHUNK;   // logits per stats block
 constexpr int kDrawThreads = 1024;
 constexpr int kDrawPer = SV_DRAW_PER; // weights per thread per draw chunk
 constexpr int kDrawChunk = kDrawThreads * kDrawPer;
-// Draw chunks summed per chain_chunks block: three on large batches (fewer,
-// fuller blocks), one when a chunk per block still fits one wave of resident
-// blocks (small batches are latency-bound: more blocks, shorter each).
-constexpr int kDrawCpbLarge = 3;
+// Draw chunks summed per chain_chunks block: one when a chunk per block still
+// fits one wave of resident blocks (small batches are latency-bound: more
+// blocks, shorter each), else five (about one block per CU, every load of the
+// block in flight at once).
+constexpr int kDrawCpbLarge = 5;
+constexpr int kDrawCpbScalar = 3;     // the scalar-load path: five would spill
 constexpr int kDrawResident = 512;    // 1024-thread blocks resident on 256 CUs
 
 __device__ __forceinline__ const float* chain_row(const ChainArgs& a, int b, int rho) {
@@ -522,13 +524,14 @@ hipError_t launch_chain(const ChainPlan& p, const float* target, const float* dr
   else chain_stats_kernel<1><<<g1, kStatsThreads, 0, st>>>(a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const dim3 g2((p.dchunks + p.cpb - 1) / p.cpb, B);
-  if (p.cpb == 1) {
+  const int cpb = p.cpb == 1 ? 1 : vec4 ? kDrawCpbLarge : kDrawCpbScalar;
+  const dim3 g2((p.dchunks + cpb - 1) / cpb, B);
+  if (cpb == 1) {
     if (vec4) chain_chunks_kernel<4, 1><<<g2, kDrawThreads, 0, st>>>(a);
     else chain_chunks_kernel<1, 1><<<g2, kDrawThreads, 0, st>>>(a);
   } else {
     if (vec4) chain_chunks_kernel<4, kDrawCpbLarge><<<g2, kDrawThreads, 0, st>>>(a);
-    else chain_chunks_kernel<1, kDrawCpbLarge><<<g2, kDrawThreads, 0, st>>>(a);
+    else chain_chunks_kernel<1, kDrawCpbScalar><<<g2, kDrawThreads, 0, st>>>(a);
   }
   e = hipGetLastError();
   if (e != hipSuccess) return e;

@@ -56,7 +56,7 @@ struct ChainPlan {
   int chunk;         // logits per stats block
   int nchunks;       // stats chunks per row
   int dchunks;       // draw chunks per row
-  int cpb;           // draw chunks per chain_chunks block
+  int cpb;           // draw chunks per chain_chunks block: 1, or more on large batches
   size_t stats_bytes, csum_bytes, decision_bytes, total_bytes;
 };
 
