@@ -416,15 +416,18 @@ def main():
 
     alphas = {}
     if not args.no_alpha and w.kind == "chain":
-        # T(N) for N = 0, 4, 8 and the workload's own N, in interleaved rounds
-        # (the box's speed drifts by a few per cent over seconds); the median
-        # step time of each N enters alpha.
+        # T(N) for N = 0, 4, 8 and the workload's own N, interleaved two steps
+        # at a time over many rounds (the box's speed drifts by a few per cent
+        # over seconds, more than alpha itself); the median step time of each
+        # N enters alpha.
         ns = sorted({0, 4, 8, w.N})
         steps_n = {n: (step if n == w.N else Step(w.with_(T=n + 1), dev)) for n in ns}
+        for n in ns:
+            time_steps(steps_n[n], 1, 2, flush)
         per_n = {n: [] for n in ns}
-        for _ in range(5):
+        for _ in range(max(40, args.steps)):
             for n in ns:
-                tn = time_steps(steps_n[n], max(10, args.steps // 5), 2, flush)
+                tn = time_steps(steps_n[n], 2, 0, flush)
                 per_n[n].append(tn["ms_per_step"])
         times = {n: pct(per_n[n], 0.5) for n in ns}
         for n in ns:
