@@ -14,7 +14,7 @@
 //                 the sequence's decision (merges the chunk statistics into
 //                 the row normalisers, runs the N ratio tests with two gathers
 //                 a row, takes the first rejection k), then sums the weights
-//                 of its chunk of the drawn row (the residual (p_k - q_k)+, or
+//                 of its chunks of the drawn row (the residual (p_k - q_k)+, or
 //                 p_N); block 0 records the decision;
 //  chain_select — one block per sequence: locates the chunk holding the
 //                 inverse-CDF crossing from the chunk sums and re-scans that
