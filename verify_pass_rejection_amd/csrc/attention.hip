@@ -618,10 +618,11 @@ void attn_mfma_kernel(AttnArgs a) {
     for (int kk = 0; kk < KK; ++kk) settle(__builtin_bit_cast(u32x4_t, qf[rt][kk]));
 
   f32x4_t acc[RT][DT];
-  float m[RT], lsum[RT];
+  float m[RT], m8[RT], lsum[RT];      // m8 = m + kRescaleLog2, the raising threshold
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) {
     m[rt] = kNegInf;
+    m8[rt] = kNegInf;
     lsum[rt] = 0.f;
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) acc[rt][dt] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
@@ -683,10 +684,17 @@ void attn_mfma_kernel(AttnArgs a) {
   // past the prefix), raises m where the tile's max exceeds it by 2^8 and
   // rescales the accumulators of those rows (rare).  sexp: probabilities as
   // bf16 in the B-operand layout of P.V (pf), their rounded sum into lsum.
+  //
+  // A row's m is raised only where the tile's row max, scaled, exceeds m by
+  // kRescaleLog2.  A lane whose own max does not exceed it cannot raise its
+  // row (max commutes with the positive scale), and a lane whose max does
+  // has the row max's value, so the cross-lane row reduction runs only when
+  // some lane of the wave exceeds the threshold: the same m as reducing on
+  // every tile, at 6 instead of 18 vector instructions per row tile.
   auto smax = [&](auto clean_tag, f32x4_t (&st)[RT][2], int base) SV_INLINE {
     constexpr bool CLEAN = decltype(clean_tag)::value;
-    float mold[RT];
-    bool raised = false;
+    float lm[RT];
+    bool hit = false;
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) {
       if constexpr (!CLEAN) {
@@ -697,21 +705,29 @@ void attn_mfma_kernel(AttnArgs a) {
         }
       }
       const f32x4_t x0 = st[rt][0], x1 = st[rt][1];
-      float mt = fmaxf(fmaxf(fmaxf(x0[0], x0[1]), fmaxf(x0[2], x0[3])),
-                       fmaxf(fmaxf(x1[0], x1[1]), fmaxf(x1[2], x1[3])));
-      mt = group4_max(mt) * c;                  // scale > 0: max commutes with scaling
-      mold[rt] = m[rt];
-      if (mt > m[rt] + kRescaleLog2) m[rt] = mt;
-      raised |= m[rt] != mold[rt];
+      lm[rt] = fmaxf(fmaxf(fmaxf(x0[0], x0[1]), fmaxf(x0[2], x0[3])),
+                     fmaxf(fmaxf(x1[0], x1[1]), fmaxf(x1[2], x1[3])));
+      hit |= lm[rt] * c > m8[rt];
     }
-    if (__any(raised)) {
+    if (__any(hit)) {
+      float mold[RT];
+      bool raised = false;
 #pragma unroll
       for (int rt = 0; rt < RT; ++rt) {
-        // unchanged rows (possibly still -inf) keep factor 1; mold = -inf gives 0
-        const float alpha = m[rt] == mold[rt] ? 1.f : fast_exp2(mold[rt] - m[rt]);
-        lsum[rt] *= alpha;
+        const float mt = group4_max(lm[rt]) * c;   // scale > 0: max commutes with scaling
+        mold[rt] = m[rt];
+        if (mt > m8[rt]) { m[rt] = mt; m8[rt] = mt + kRescaleLog2; }
+        raised |= m[rt] != mold[rt];
+      }
+      if (__any(raised)) {
 #pragma unroll
-        for (int dt = 0; dt < DT; ++dt) acc[rt][dt] *= alpha;
+        for (int rt = 0; rt < RT; ++rt) {
+          // unchanged rows (possibly still -inf) keep factor 1; mold = -inf gives 0
+          const float alpha = m[rt] == mold[rt] ? 1.f : fast_exp2(mold[rt] - m[rt]);
+          lsum[rt] *= alpha;
+#pragma unroll
+          for (int dt = 0; dt < DT; ++dt) acc[rt][dt] *= alpha;
+        }
       }
     }
   };
