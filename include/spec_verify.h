@@ -66,6 +66,8 @@ typedef enum {
 /* Supported limits. */
 #define SPEC_MAX_T 64          /* query positions (chain N+1, or tree nodes)      */
 #define SPEC_MAX_V (1 << 24)   /* vocabulary size                                 */
+#define SPEC_MAX_ROWS 65535    /* B·Hkv (attention), B·(2N+1) (chain), B·T (trees),
+                                  B (n-gram): one launch-grid axis each            */
 
 /* Text for a status code (static storage; never NULL). */
 const char* spec_status_string(spec_status status);
@@ -90,8 +92,9 @@ const char* spec_status_string(spec_status status);
  *   out      [B, T, Hq, D] float32
  *   scale    softmax scale, normally 1/sqrt(D); must be finite and > 0
  *
- * Limits: 1 <= T <= 64, D in {64, 128}, Hkv >= 1, Hq % Hkv == 0, ctx >= 0;
- * q, k, v and out 16-byte aligned (SPEC_ERR_UNSUPPORTED otherwise).
+ * Limits: 1 <= T <= 64, D in {64, 128}, Hkv >= 1, Hq % Hkv == 0, ctx >= 0,
+ * B·Hkv <= SPEC_MAX_ROWS; q, k, v and out 16-byte aligned (SPEC_ERR_UNSUPPORTED
+ * otherwise).
  * ------------------------------------------------------------------------- */
 size_t spec_verify_attention_workspace(int B, int T, int Hq, int Hkv, int D, int ctx,
                                        spec_dtype dtype);
@@ -178,7 +181,7 @@ spec_status spec_verify_attention_paged(const void* q, const void* k_pages, cons
  *   out_tokens     [B, N+1]    int32 out: x_0..x_{k-1}, y, then -1
  *
  * For N == 0 the pointers to draft_logits, draft_tokens and u_accept may be NULL.
- * Limits: N >= 0, 1 <= V <= SPEC_MAX_V.
+ * Limits: N >= 0, 1 <= V <= SPEC_MAX_V, B·(2N+1) <= SPEC_MAX_ROWS.
  * ------------------------------------------------------------------------- */
 size_t spec_accept_chain_workspace(int B, int N, int V);
 
@@ -206,7 +209,7 @@ spec_status spec_accept_chain(const float* target_logits, const float* draft_log
  *   path           [B, T]     int32 out: node ids root..l, then -1
  *   out_tokens     [B, T]     int32 out: tokens of path nodes 1..l, then a_l, then -1
  *
- * Limits: 1 <= T <= 64, 1 <= V <= SPEC_MAX_V.
+ * Limits: 1 <= T <= 64, 1 <= V <= SPEC_MAX_V, B·T <= SPEC_MAX_ROWS.
  * ------------------------------------------------------------------------- */
 size_t spec_accept_tree_workspace(int B, int T, int V);
 
@@ -247,7 +250,8 @@ spec_status spec_accept_tree(const float* target_logits, const int32_t* tokens,
  *
  * Precision: probabilities from float32-accurate exponentials (an exact
  * float64 argument split around the hardware exp2), every sum, ratio and
- * comparison in float64.  Limits: 1 <= T <= 64, 1 <= V <= SPEC_MAX_V.
+ * comparison in float64.  Limits: 1 <= T <= 64, 1 <= V <= SPEC_MAX_V,
+ * B·T <= SPEC_MAX_ROWS.
  * ------------------------------------------------------------------------- */
 size_t spec_accept_tree_sampled_workspace(int B, int T, int V);
 
@@ -276,7 +280,8 @@ spec_status spec_accept_tree_sampled(const float* target_logits, const float* dr
  *   num_drafts    [B] int32 out: number of drafts (0..N)
  *   drafts        [B, N] int32 out: the drafts, then -1
  *
- * Limits: 0 <= N <= SPEC_MAX_T - 1, 1 <= n_min <= n_max <= SPEC_NGRAM_MAX.
+ * Limits: 0 <= N <= SPEC_MAX_T - 1, 1 <= n_min <= n_max <= SPEC_NGRAM_MAX,
+ * B <= SPEC_MAX_ROWS.
  * Workspace: spec_ngram_propose_workspace(B, L).
  * ------------------------------------------------------------------------- */
 #define SPEC_NGRAM_MAX 16
