@@ -66,8 +66,8 @@ typedef enum {
 /* Supported limits. */
 #define SPEC_MAX_T 64          /* query positions (chain N+1, or tree nodes)      */
 #define SPEC_MAX_V (1 << 24)   /* vocabulary size                                 */
-#define SPEC_MAX_ROWS 65535    /* B·Hkv (attention), B·(2N+1) (chain), B·T (trees),
-                                  B (n-gram): one launch-grid axis each            */
+#define SPEC_MAX_ROWS 0x7fffffff /* B·Hkv (attention), B·(2N+1) (chain), B·T (trees):
+                                    block indices are 32-bit signed               */
 
 /* Text for a status code (static storage; never NULL). */
 const char* spec_status_string(spec_status status);
@@ -280,8 +280,7 @@ spec_status spec_accept_tree_sampled(const float* target_logits, const float* dr
  *   num_drafts    [B] int32 out: number of drafts (0..N)
  *   drafts        [B, N] int32 out: the drafts, then -1
  *
- * Limits: 0 <= N <= SPEC_MAX_T - 1, 1 <= n_min <= n_max <= SPEC_NGRAM_MAX,
- * B <= SPEC_MAX_ROWS.
+ * Limits: 0 <= N <= SPEC_MAX_T - 1, 1 <= n_min <= n_max <= SPEC_NGRAM_MAX.
  * Workspace: spec_ngram_propose_workspace(B, L).
  * ------------------------------------------------------------------------- */
 #define SPEC_NGRAM_MAX 16

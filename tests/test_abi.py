@@ -67,8 +67,8 @@ def test_attention_validation():
     assert attn(ws_bytes=16) == WS
     assert attn(q=FAKE + 4) == UNSUP         # 16-byte loads and stores need alignment
     assert attn(out=FAKE + 8) == UNSUP
-    assert attn(B=40000, Hkv=2) == UNSUP     # B*Hkv above SPEC_MAX_ROWS (one grid axis)
-    assert attn(B=32767, Hkv=2, q=None) == NULL
+    assert attn(B=1 << 30, Hkv=2) == UNSUP   # B*Hkv past int32 block ids
+    assert attn(B=(1 << 30) - 1, Hkv=2, q=None) == NULL
     assert attn(B=0, q=None) == OK          # empty problem: nothing launched
     assert attn(T=0, q=None) == OK
 
@@ -142,8 +142,8 @@ def test_chain_validation():
     assert chain(N=64) == UNSUP
     assert chain(V=(1 << 24) + 1) == UNSUP
     assert chain(ws_bytes=8) == WS
-    assert chain(B=10000, N=3) == UNSUP      # B*(2N+1) above SPEC_MAX_ROWS
-    assert chain(B=9362, N=3, t=None) == NULL
+    assert chain(B=1 << 29, N=3) == UNSUP    # B*(2N+1) past int32 block ids
+    assert chain(B=(2**31 - 1) // 7, N=3, t=None) == NULL
     assert chain(B=0, t=None) == OK
     # N = 0 needs no draft rows, tokens or accept uniforms
     assert chain(N=0, d=None, x=None, ua=None, ws_bytes=8) == WS
@@ -169,8 +169,8 @@ def test_tree_validation():
     assert tree(T=65) == UNSUP
     assert tree(V=0) == SHAPE
     assert tree(ws_bytes=4) == WS
-    assert tree(B=7000, T=10) == UNSUP       # B*T above SPEC_MAX_ROWS
-    assert tree(B=6553, T=10, par=None) == NULL
+    assert tree(B=1 << 27, T=16) == UNSUP    # B*T past int32 block ids
+    assert tree(B=(1 << 27) - 1, T=16, par=None) == NULL
     assert tree(B=0, z=None) == OK
     assert nat.spec_accept_tree_workspace(8, 64, 32000) > 0
 
@@ -217,8 +217,8 @@ def test_sampled_tree_validation():
     assert stree(V=(1 << 24) + 1) == UNSUP
     assert stree(ws=None) == NULL
     assert stree(ws_bytes=8) == WS
-    assert stree(B=7000, T=10) == UNSUP
-    assert stree(B=6553, T=10, t=None) == NULL
+    assert stree(B=1 << 27, T=16) == UNSUP
+    assert stree(B=(1 << 27) - 1, T=16, t=None) == NULL
     assert stree(B=0, t=None) == OK
     assert stree(T=0, t=None) == OK
     f = nat.spec_accept_tree_sampled_workspace
@@ -248,8 +248,6 @@ def test_ngram_validation():
     assert ngram(N=64) == UNSUP
     assert ngram(n_max=17) == UNSUP
     assert ngram(ws_bytes=8) == WS
-    assert ngram(B=65536) == UNSUP
-    assert ngram(B=65535, c=None) == NULL
     assert ngram(B=0, c=None) == OK
     f = nat.spec_ngram_propose_workspace
     assert f(64, 32768) >= 64 * 8 * 8 and f(64, 32768) % 256 == 0

@@ -309,9 +309,12 @@ __device__ __forceinline__ int chain_decision(const ChainArgs& a, int b, float* 
 }
 
 // The drawn row's weights for sequence b, from the decision record.
+// Both records are loaded whatever k is, so that neither load waits for the
+// other.
 __device__ __forceinline__ void draw_rows(const ChainArgs& a, int b, int& k, DrawRow& dp,
                                           DrawRow& dr) {
   const float4 dec = a.decision[b];
+  const float4 dq = a.decision_q[b];
   k = __float_as_int(dec.x);
   dp.zp = a.target + ((size_t)b * (a.N + 1) + k) * a.V;
   dp.mp = dec.y;
@@ -321,7 +324,6 @@ __device__ __forceinline__ void draw_rows(const ChainArgs& a, int b, int& k, Dra
   dp.mq = dp.lq = 0.f;
   dr = dp;
   if (k < a.N) {
-    const float4 dq = a.decision_q[b];
     dr.zq = a.draft + ((size_t)b * a.N + k) * a.V;
     dr.mq = dq.x;
     dr.lq = dq.y;
@@ -386,6 +388,10 @@ __global__ __launch_bounds__(kDrawThreads) void chain_select_kernel(ChainArgs a)
   __shared__ float s_carry, s_target;
   const int b = blockIdx.x, tid = threadIdx.x, N = a.N, nch = a.dchunks;
   const int lane = tid & 63, wave = tid >> 6;
+  // The sequence's draw uniforms, its decision records and the chunk sums
+  // are independent loads, issued together; u is picked once k is known.
+  __shared__ float u_l[64];                // N + 1 <= 64, checked on the host
+  if (tid <= N) u_l[tid] = a.u_draw[(size_t)b * (N + 1) + tid];
   int k;
   DrawRow dp, dr;
   draw_rows(a, b, k, dp, dr);
@@ -394,8 +400,8 @@ __global__ __launch_bounds__(kDrawThreads) void chain_select_kernel(ChainArgs a)
   __shared__ float cs_l[kDrawThreads];
   const bool in_lds = nch <= kDrawThreads;
   if (in_lds && tid < nch) cs_l[tid] = cs[tid];           // one parallel load
-  const float u = a.u_draw[(size_t)b * (N + 1) + k];
   __syncthreads();
+  const float u = u_l[k];
 
   if (tid == 0) {
     float total = 0.f;

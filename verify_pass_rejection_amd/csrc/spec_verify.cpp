@@ -46,7 +46,7 @@ spec_status check_attention(int B, int T, int Hq, int Hkv, int D, int ctx, spec_
   if (T > SPEC_MAX_T || (D != 64 && D != 128)) return SPEC_ERR_UNSUPPORTED;
   // keep every element index of K/V below 2^31 per (sequence, KV head) unit
   if ((long long)(ctx + T) * D >= (1ll << 31)) return SPEC_ERR_UNSUPPORTED;
-  if ((long long)B * Hkv > SPEC_MAX_ROWS) return SPEC_ERR_UNSUPPORTED;   // grid axis
+  if ((long long)B * Hkv > SPEC_MAX_ROWS) return SPEC_ERR_UNSUPPORTED;   // int32 block ids
   return SPEC_OK;
 }
 
@@ -60,7 +60,6 @@ spec_status check_chain(int B, int N, int V) {
 spec_status check_ngram(int B, int L, int N, int n_min, int n_max) {
   if (B < 0 || L < 0 || N < 0 || n_min < 1 || n_max < n_min) return SPEC_ERR_SHAPE;
   if (N > SPEC_MAX_T - 1 || n_max > SPEC_NGRAM_MAX) return SPEC_ERR_UNSUPPORTED;
-  if (B > SPEC_MAX_ROWS) return SPEC_ERR_UNSUPPORTED;
   return SPEC_OK;
 }
 
