@@ -1,0 +1,134 @@
+"""GPU parity over seeded random shapes, beyond the hand-picked edge cases.
+
+Each case draws its sizes from a fixed seed: batch, query positions, head
+counts and grouping, head dimension, prefix length (including 0), fp32 or
+bf16, chain or a random tree (every node's parent uniform over the earlier
+nodes, so branches of any depth and width occur); vocabulary sizes that are
+and are not multiples of 4, temperatures other than 1.  Attention is compared
+element by element with oracle.attention (max-abs 1e-4 fp32, 2e-2 bf16); chain
+acceptance exactly on every unflagged sequence (band 1e-6), greedy tree
+acceptance exactly.
+"""
+import numpy as np
+import pytest
+import torch
+
+from gpu_support import BF16_ATOL, F32_ATOL, device, f64, i64, say
+from oracle.accept import chain_accept, tree_accept
+from oracle.attention import verify_attention
+from verify_pass_rejection_amd import inputs as I
+from verify_pass_rejection_amd import native as nat
+
+pytestmark = pytest.mark.gpu
+
+
+def random_parents(B: int, T: int, g: torch.Generator) -> torch.Tensor:
+    """[B, T] int32: parent of node 0 is -1, parent of node i uniform in [0, i)."""
+    par = torch.full((B, T), -1, dtype=torch.int32)
+    for i in range(1, T):
+        par[:, i] = torch.randint(0, i, (B,), generator=g, dtype=torch.int32)
+    return par
+
+
+def attention_case(seed: int):
+    g = torch.Generator().manual_seed(1000 + seed)
+    pick = lambda xs: xs[int(torch.randint(0, len(xs), (1,), generator=g))]   # noqa: E731
+    D = pick([64, 128])
+    Hkv = pick([1, 2, 4, 8])
+    G = pick([1, 2, 4, 8])
+    T = int(torch.randint(1, 65, (1,), generator=g))
+    ctx = pick([0, 1, 31, 32, 33, 257, 1000, 1999])
+    B = int(torch.randint(1, 4, (1,), generator=g))
+    dtype = pick(["bf16", "bf16", "f32"])
+    tree = bool(torch.randint(0, 2, (1,), generator=g))
+    return dict(D=D, Hkv=Hkv, Hq=G * Hkv, T=T, ctx=ctx, B=B, dtype=dtype, tree=tree,
+                g=g)
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_attention_random_shapes(seed):
+    dev = device()
+    c = attention_case(seed)
+    w = I.WORKLOADS["large_batch_chain"].with_(
+        name=f"random_{seed}", kind="chain", B=c["B"], T=c["T"], Hq=c["Hq"], Hkv=c["Hkv"],
+        D=c["D"], ctx=c["ctx"], dtype=c["dtype"], seed=200 + seed)
+    q, k, v = I.make_attention_inputs(w, dev)
+    par = random_parents(w.B, w.T, c["g"]) if c["tree"] else None
+    say(w.name, f"B={w.B} T={w.T} Hq={w.Hq} Hkv={w.Hkv} D={w.D} ctx={w.ctx} {w.dtype}",
+        "tree" if c["tree"] else "chain")
+    out = nat.spec_verify_attention(q, k, v, w.ctx,
+                                    parents=None if par is None else par.to(dev))
+    torch.cuda.synchronize()
+    want = verify_attention(f64(q), f64(k), f64(v), w.ctx,
+                            parents=None if par is None else par.numpy().astype(np.int64))
+    got = f64(out)
+    tol = F32_ATOL if w.dtype == "f32" else BF16_ATOL
+    err = float(np.max(np.abs(got - want)))
+    say(w.name, f"max_abs_err={err:.3e} tol={tol}")
+    assert np.all(np.isfinite(got))
+    assert err <= tol
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_chain_acceptance_random_shapes(seed):
+    dev = device()
+    g = torch.Generator().manual_seed(3000 + seed)
+    B = int(torch.randint(1, 65, (1,), generator=g))
+    N = int(torch.randint(0, 13, (1,), generator=g))
+    V = [7, 1000, 4099, 8192, 8196, 16385, 40000, 131071][seed]
+    tau = [0.6, 1.0, 1.5, 1.0, 0.8, 1.0, 2.0, 1.0][seed]
+    w = I.WORKLOADS["large_batch_chain"].with_(B=B, T=N + 1, V=V, temperature=tau,
+                                               seed=400 + seed)
+    d = I.make_chain_inputs(w, dev)
+    num, out = nat.spec_accept_chain(d["target_logits"], d["draft_logits"], d["draft_tokens"],
+                                     d["u_accept"], d["u_draw"], temperature=tau)
+    torch.cuda.synchronize()
+    ref = chain_accept(f64(d["target_logits"]), f64(d["draft_logits"]), i64(d["draft_tokens"]),
+                       f64(d["u_accept"]), f64(d["u_draw"]), temperature=tau, band=1e-6)
+    num, out = i64(num), i64(out)
+    ok = ~ref.near_boundary
+    mism = ok & ((num != ref.num_accepted) | np.any(out != ref.out_tokens, axis=1))
+    say(f"chain seed {seed}", f"B={B} N={N} V={V} tau={tau}",
+        f"flagged={int((~ok).sum())} mismatched={int(mism.sum())}")
+    assert not mism.any(), np.nonzero(mism)[0][:10]
+    # the emitted prefix is the drafts, then one token in range, then -1
+    for b in np.nonzero(ok)[0]:
+        k = num[b]
+        assert 0 <= k <= N
+        assert np.array_equal(out[b, :k], i64(d["draft_tokens"])[b, :k])
+        assert 0 <= out[b, k] < V and np.all(out[b, k + 1:] == -1)
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_tree_acceptance_random_trees(seed):
+    dev = device()
+    g = torch.Generator().manual_seed(5000 + seed)
+    B = int(torch.randint(1, 17, (1,), generator=g))
+    T = int(torch.randint(1, 65, (1,), generator=g))
+    V = [3, 1000, 4097, 32000, 50001, 8][seed]
+    par = random_parents(B, T, g)
+    logits = torch.randn((B, T, V), generator=g) * 3
+    # the first child of each node carries its parent's most likely token with
+    # probability 0.7 (a plant: that logit is raised above the row), other
+    # children random tokens; small V also produces ties and duplicate siblings
+    tokens = torch.randint(0, V, (B, T), generator=g, dtype=torch.int32)
+    for b in range(B):
+        seen = set()
+        for i in range(1, T):
+            p = int(par[b, i])
+            if p not in seen and float(torch.rand(1, generator=g)) < 0.7:
+                t = int(torch.randint(0, V, (1,), generator=g))
+                logits[b, p, t] = float(logits[b, p].max()) + 1.0
+                tokens[b, i] = t
+            seen.add(p)
+    if V <= 8:
+        logits = torch.round(logits)          # equal maxima: the lowest token wins
+    al, path, out = nat.spec_accept_tree(logits.to(dev), tokens.to(dev), par.to(dev))
+    torch.cuda.synchronize()
+    ref = tree_accept(logits.double().numpy(), tokens.numpy().astype(np.int64),
+                      par.numpy().astype(np.int64))
+    say(f"tree seed {seed}", f"B={B} T={T} V={V}",
+        f"mean_accept_len={i64(al).mean():.2f}")
+    np.testing.assert_array_equal(i64(al), ref.accept_len)
+    np.testing.assert_array_equal(i64(path), ref.path)
+    np.testing.assert_array_equal(i64(out), ref.out_tokens)
