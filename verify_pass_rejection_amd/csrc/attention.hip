@@ -741,7 +741,7 @@ void attn_mfma_kernel(AttnArgs a) {
       const f32x4_t x0 = st[rt][0], x1 = st[rt][1];
       const float sc[8] = {x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
       bf16x2_t pk[4];
-      float sum = 0.f;
+      float sum = lsum[rt];
 #pragma unroll
       for (int e = 0; e < 8; e += 2) {
         const float p0 = fast_exp2(fmaf(sc[e], c, -msub));
@@ -749,7 +749,7 @@ void attn_mfma_kernel(AttnArgs a) {
         pk[e / 2] = __builtin_convertvector((f32x2_t){p0, p1}, bf16x2_t);
         sum = __builtin_amdgcn_fdot2_f32_bf16(pk[e / 2], ones, sum, false);
       }
-      lsum[rt] += sum;
+      lsum[rt] = sum;
       pf[rt] = __builtin_shufflevector(__builtin_shufflevector(pk[0], pk[1], 0, 1, 2, 3),
                                        __builtin_shufflevector(pk[2], pk[3], 0, 1, 2, 3),
                                        0, 1, 2, 3, 4, 5, 6, 7);
