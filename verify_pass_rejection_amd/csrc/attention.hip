@@ -420,9 +420,10 @@ struct MfmaRing {
   // LAG: with two compute waves per SIMD (more than four compute waves), the
   // upper waves run half a tile behind (see the key loop), which keeps the
   // previous tile's slot in use until the next barrier.  Measured: medusa
-  // tree (three row tiles) 115-118 -> 111 us; eagle2 tree (two row tiles)
-  // 95-98 -> 104-106 us, so only three-row-tile kernels lag.
-  static constexpr bool LAG = RT == 3 && SV_MFMA_LAG;
+  // tree (three row tiles) 104.8 -> 97.8 us; eagle2 tree (two row tiles)
+  // 94.8 -> 91.8 us once the softmax had shed its per-tile row reduction
+  // (before that, two-row-tile kernels were slower lagged).
+  static constexpr bool LAG = RT >= 2 && SV_MFMA_LAG;
   static constexpr int P = RT == 1 ? 4 : LAG ? 6 : 5;
   static constexpr int AHEAD_MAX = 63 / MfmaLayout<D>::NIT + 1;   // (AHEAD-1)*NIT < 64
   static constexpr int AHEAD = (LAG ? P - 2 : P - 1) < AHEAD_MAX ? (LAG ? P - 2 : P - 1)
