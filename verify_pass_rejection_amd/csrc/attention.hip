@@ -686,12 +686,12 @@ void attn_mfma_kernel(AttnArgs a) {
   // rescales the accumulators of those rows (rare).  sexp: probabilities as
   // bf16 in the B-operand layout of P.V (pf), their rounded sum into lsum.
   //
-  // A row's m is raised only where the tile's row max, scaled, exceeds m by
-  // kRescaleLog2.  A lane whose own max does not exceed it cannot raise its
-  // row (max commutes with the positive scale), and a lane whose max does
-  // has the row max's value, so the cross-lane row reduction runs only when
-  // some lane of the wave exceeds the threshold: the same m as reducing on
-  // every tile, at 6 instead of 18 vector instructions per row tile.
+  // A row's m is raised only where the tile's row max, scaled, exceeds
+  // m8 = m + kRescaleLog2.  The scaled row max exceeds m8 exactly when some
+  // lane's own scaled max does (max commutes with the positive scale), so the
+  // cross-lane row reduction runs only when some lane of the wave passes that
+  // check: m evolves exactly as with a reduction on every tile, at 6 instead
+  // of 18 vector instructions per row tile.
   auto smax = [&](auto clean_tag, f32x4_t (&st)[RT][2], int base) SV_INLINE {
     constexpr bool CLEAN = decltype(clean_tag)::value;
     float lm[RT];
