@@ -1,0 +1,66 @@
+"""The measurement model of bench.py, on the host: algorithmic bytes and flops
+per call against the per-configuration table worked out by hand from the
+workload shapes (K and V of every key once, Q once, the fp32 output once;
+every logit once), the per-position overhead alpha, the multi-GPU refusal, and
+the HBM-traffic figure, which is reported only while the profiled kernel
+source is unchanged."""
+import os
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+
+import bench  # noqa: E402
+from verify_pass_rejection_amd import inputs as I  # noqa: E402
+
+# (attention bytes, attention GFLOP rounded, acceptance bytes), from the shapes:
+#   tiny:   2·1·8·260·64·4 + 1·5·8·64·4 + 1·5·8·64·4
+#   llama3: 2·1·8·4102·128·2 + 6·32·128·2 + 6·32·128·4
+#   eagle2: 2·8·8·8256·128·2 + 8·64·32·128·(2+4); acceptance 8·64·32000·4
+#   medusa: 2·32·8·2090·128·2 + 32·42·64·128·(2+4); acceptance 32·42·32000·4
+#   large:  2·64·8·32777·128·2 + 64·9·32·128·(2+4); acceptance 64·17·152064·4
+TABLE = {
+    "tiny_chain": (1_089_536, 0.0027, 36_864),
+    "llama3_8b_chain": (16_949_248, 0.403, 5_643_264),
+    "eagle2_tree": (283_115_520, 69.26, 65_536_000),
+    "medusa70b_tree": (340_000_768, 92.04, 172_032_000),
+    "large_batch_chain": (8_606_449_664, 309.3, 661_782_528),
+}
+
+
+@pytest.mark.parametrize("name", list(TABLE))
+def test_algorithmic_bytes_and_flops(name):
+    w = I.WORKLOADS[name]
+    attn, gflop, acc = TABLE[name]
+    assert bench.attention_bytes(w) == attn
+    assert bench.sampler_bytes(w) == acc
+    assert bench.attention_flops(w) / 1e9 == pytest.approx(gflop, rel=2e-3)
+
+
+def test_alpha_is_the_per_position_overhead():
+    # T(N) = T(0) (1 + N alpha)
+    assert bench.alpha(1.2, 1.0, 4) == pytest.approx(0.05)
+    assert bench.alpha(1.0, 1.0, 8) == 0.0
+    assert bench.alpha(1.074, 1.0, 8) == pytest.approx(0.00925)
+
+
+def test_more_than_one_gpu_is_refused_with_a_message():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=300)
+    assert "one GPU" in (r.stdout + r.stderr)
+
+
+def test_traffic_is_reported_only_for_the_profiled_source(tmp_path, monkeypatch):
+    got = bench.measured_traffic()
+    assert got is not None
+    # the two counter passes, scaled by the copy calibration, come close to the
+    # algorithmic bytes of the launch (no re-reads)
+    algo = bench.attention_bytes(I.WORKLOADS["large_batch_chain"])
+    assert abs(got - algo) / algo < 0.01
+    changed = tmp_path / "attention.hip"
+    changed.write_text(open(bench.ATTN_SOURCE).read() + "\n// edited\n")
+    monkeypatch.setattr(bench, "ATTN_SOURCE", str(changed))
+    assert bench.measured_traffic() is None
