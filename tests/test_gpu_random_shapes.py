@@ -5,9 +5,10 @@ counts and grouping, head dimension, prefix length (including 0), fp32 or
 bf16, chain or a random tree (every node's parent uniform over the earlier
 nodes, so branches of any depth and width occur); vocabulary sizes that are
 and are not multiples of 4, temperatures other than 1.  Attention is compared
-element by element with oracle.attention (max-abs 1e-4 fp32, 2e-2 bf16); chain
-acceptance exactly on every unflagged sequence (band 1e-6), greedy tree
-acceptance exactly.
+element by element with oracle.attention (max-abs 1e-4 fp32, 2e-2 bf16), and
+over a paged cache (ragged prefix lengths, page sizes 1-256, both layouts) with
+oracle.paged; chain acceptance exactly on every unflagged sequence (band 1e-6),
+greedy tree acceptance exactly.
 """
 import numpy as np
 import pytest
@@ -132,3 +133,37 @@ def test_tree_acceptance_random_trees(seed):
     np.testing.assert_array_equal(i64(al), ref.accept_len)
     np.testing.assert_array_equal(i64(path), ref.path)
     np.testing.assert_array_equal(i64(out), ref.out_tokens)
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_paged_attention_random_shapes(seed):
+    """Paged cache with ragged prefix lengths, random trees or chains, random
+    page sizes and layouts, compared element by element with oracle.paged."""
+    from oracle.paged import verify_attention_paged
+    dev = device()
+    c = attention_case(100 + seed)
+    g = c["g"]
+    page_size = [1, 2, 4, 8, 16, 32, 64, 256][int(torch.randint(0, 8, (1,), generator=g))]
+    layout = ["hnd", "nhd"][seed % 2]
+    w = I.WORKLOADS["large_batch_chain"].with_(
+        name=f"paged_random_{seed}", kind="chain", B=max(c["B"], 2), T=c["T"], Hq=c["Hq"],
+        Hkv=c["Hkv"], D=c["D"], ctx=max(c["ctx"], 1), dtype=c["dtype"], seed=600 + seed)
+    q, k, v = I.make_attention_inputs(w, dev)
+    par = random_parents(w.B, w.T, g) if c["tree"] else None
+    lens = I.ragged_ctx_lens(w, dev)
+    kp, vp, bt = I.make_paged_kv(w, k, v, page_size, layout, lens.cpu())
+    say(w.name, f"B={w.B} T={w.T} Hq={w.Hq} Hkv={w.Hkv} D={w.D} ctx={w.ctx} {w.dtype}",
+        f"ps={page_size} {layout} lens={lens.cpu().tolist()}", "tree" if c["tree"] else "chain")
+    out = nat.spec_verify_attention_paged(q, kp, vp, bt, w.ctx, ctx_lens=lens,
+                                          parents=None if par is None else par.to(dev),
+                                          layout=layout)
+    torch.cuda.synchronize()
+    want = verify_attention_paged(f64(q), f64(kp), f64(vp), bt.cpu().numpy(),
+                                  lens.cpu().numpy(),
+                                  None if par is None else par.numpy().astype(np.int64), layout)
+    got = f64(out)
+    tol = F32_ATOL if w.dtype == "f32" else BF16_ATOL
+    err = float(np.max(np.abs(got - want)))
+    say(w.name, f"max_abs_err={err:.3e} tol={tol}")
+    assert np.all(np.isfinite(got))
+    assert err <= tol
