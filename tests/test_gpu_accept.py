@@ -51,6 +51,8 @@ def compare_chain(d, temperature=1.0, label=""):
     ("large_batch_chain", dict(B=16, V=1001)),      # V not a multiple of 4: scalar path
     ("large_batch_chain", dict(B=64, T=1)),         # N = 0: plain sampling from p_0
     ("large_batch_chain", dict(B=32, T=64, V=777)), # N = 63
+    ("large_batch_chain", dict(B=16, T=5, V=1)),    # one token: every draft kept
+    ("large_batch_chain", dict(B=16, T=9, V=2)),
 ])
 def test_chain_matches_oracle(name, kw):
     dev = device()
@@ -120,6 +122,8 @@ def compare_tree(d, label=""):
     ("medusa70b_tree", dict()),              # full reference size
     ("eagle2_tree", dict(B=4, V=3001)),      # ragged vocabulary, scalar path
     ("medusa70b_tree", dict(B=8, V=20000, seed=31)),
+    ("eagle2_tree", dict(B=2, V=1)),         # one token: the whole tree agrees
+    ("medusa70b_tree", dict(B=4, V=2)),
 ])
 def test_tree_matches_oracle(name, kw):
     dev = device()

@@ -236,7 +236,8 @@ def make_tree_inputs(w: Workload, device="cpu"):
             if planted:
                 logits[b, node, t] = spike
             for c in ch[1:]:
-                while int(tokens[b, c]) == t:
+                # siblings get other tokens (with one token there is no other)
+                while V > 1 and int(tokens[b, c]) == t:
                     tokens[b, c] = int(torch.randint(0, V, (1,), generator=gk))
     return dict(target_logits=logits, tokens=tokens.to(torch.int32).to(device),
                 parents=parents.to(device))
