@@ -69,6 +69,9 @@ def test_attention_validation():
     assert attn(out=FAKE + 8) == UNSUP
     assert attn(B=1 << 30, Hkv=2) == UNSUP   # B*Hkv past int32 block ids
     assert attn(B=(1 << 30) - 1, Hkv=2, q=None) == NULL
+    assert attn(ctx=(1 << 24) - 5, T=5) == UNSUP   # (ctx+T)*D = 2^31: K/V element index
+    assert attn(ctx=(1 << 24) - 6, T=5, q=None) == NULL
+    assert attn(ctx=(1 << 31) - 2, T=5) == UNSUP    # ctx + T past int32, no overflow
     assert attn(B=0, q=None) == OK          # empty problem: nothing launched
     assert attn(T=0, q=None) == OK
 
@@ -263,6 +266,7 @@ def test_commit_validation():
     assert commit(ctx=-1) == SHAPE
     assert commit(T=65) == UNSUP
     assert commit(D=32) == UNSUP
+    assert commit(ctx=(1 << 31) - 2) == UNSUP      # ctx + T past int32, no overflow
     assert commit(dtype=3) == UNSUP
     assert commit(v=FAKE + 8) == UNSUP         # 16-byte vectors
     assert commit(B=0, acc=None) == OK         # empty problem: nothing launched

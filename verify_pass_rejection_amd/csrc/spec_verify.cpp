@@ -45,7 +45,7 @@ spec_status check_attention(int B, int T, int Hq, int Hkv, int D, int ctx, spec_
   if (dtype != SPEC_F32 && dtype != SPEC_BF16) return SPEC_ERR_UNSUPPORTED;
   if (T > SPEC_MAX_T || (D != 64 && D != 128)) return SPEC_ERR_UNSUPPORTED;
   // keep every element index of K/V below 2^31 per (sequence, KV head) unit
-  if ((long long)(ctx + T) * D >= (1ll << 31)) return SPEC_ERR_UNSUPPORTED;
+  if (((long long)ctx + T) * D >= (1ll << 31)) return SPEC_ERR_UNSUPPORTED;
   if ((long long)B * Hkv > SPEC_MAX_ROWS) return SPEC_ERR_UNSUPPORTED;   // int32 block ids
   return SPEC_OK;
 }
@@ -255,7 +255,7 @@ spec_status spec_commit_kv(void* k, void* v, const int32_t* path, const int32_t*
   if (B < 0 || T < 1 || Hkv < 1 || D < 1 || ctx < 0) return SPEC_ERR_SHAPE;
   if (dtype != SPEC_F32 && dtype != SPEC_BF16) return SPEC_ERR_UNSUPPORTED;
   if (T > SPEC_MAX_T || (D != 64 && D != 128)) return SPEC_ERR_UNSUPPORTED;
-  if ((long long)(ctx + T) * D >= (1ll << 31)) return SPEC_ERR_UNSUPPORTED;
+  if (((long long)ctx + T) * D >= (1ll << 31)) return SPEC_ERR_UNSUPPORTED;
   if (B == 0) return SPEC_OK;
   if (!accept_len || !new_len) return SPEC_ERR_NULL;
   if (path != nullptr) {
