@@ -139,6 +139,8 @@ __device__ __forceinline__ void launder(float (&r)[N]) {
 // ---------------------------------------------------------------------------
 // stree_stats: block (chunk, row, kind); kind 0 = target rows, 1 = draft rows
 // (skipped for nodes without children: their draft rows are never used).
+// Ordinary (cached) loads: the walk reads the rows of the visited nodes again
+// right after this pass, and finds them in the last-level cache.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(kSTThreads) void stree_stats_kernel(STreeArgs a) {
   __shared__ double red[kSTWaves];
@@ -158,7 +160,7 @@ __global__ __launch_bounds__(kSTThreads) void stree_stats_kernel(STreeArgs a) {
 #pragma unroll
   for (int i = 0; i < PER; ++i) {
     const int v = begin + i * kSTThreads + threadIdx.x;
-    x[i] = v < end ? __builtin_nontemporal_load(z + v) : -__builtin_huge_valf();
+    x[i] = v < end ? z[v] : -__builtin_huge_valf();
   }
   float mx = x[0];
 #pragma unroll
