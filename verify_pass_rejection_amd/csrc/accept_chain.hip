@@ -73,18 +73,23 @@ __device__ __forceinline__ const float* chain_row(const ChainArgs& a, int b, int
                     : a.draft + ((size_t)b * a.N + (rho - a.N - 1)) * a.V;
 }
 
-#ifndef SV_STATS_NT
-#define SV_STATS_NT 1
-#endif
-// Logits are read once by the statistics pass.
+// The statistics pass reads every logit once; chain_chunks then reads the one
+// drawn row of each sequence again.  When all the logits fit well inside the
+// 256 MB last-level cache, ordinary loads leave the drawn rows there (0.9 of
+// 20 us on a one-sequence chain of 11 rows of 128256); a larger stream takes
+// non-temporal loads, which keep it at full rate (8 of 130 us on 64 x 17 rows
+// of 152064).
+constexpr size_t kCachedLogitBytes = size_t(128) << 20;
+
+template <bool NT>
 __device__ __forceinline__ float4 load_stream4(const float* p) {
-#if SV_STATS_NT
-  typedef float f32x4_nt __attribute__((ext_vector_type(4)));
-  const f32x4_nt v = __builtin_nontemporal_load((const f32x4_nt*)p);
-  return make_float4(v[0], v[1], v[2], v[3]);
-#else
-  return *(const float4*)p;
-#endif
+  if constexpr (NT) {
+    typedef float f32x4_nt __attribute__((ext_vector_type(4)));
+    const f32x4_nt v = __builtin_nontemporal_load((const f32x4_nt*)p);
+    return make_float4(v[0], v[1], v[2], v[3]);
+  } else {
+    return *(const float4*)p;
+  }
 }
 
 #ifndef SV_DRAW_NT
@@ -108,7 +113,7 @@ __device__ __forceinline__ void merge_ms(float& m, float& s, float m2, float s2,
   m = mx;
 }
 
-template <int VEC>
+template <int VEC, bool NT>
 __global__ __launch_bounds__(kStatsThreads) void chain_stats_kernel(ChainArgs a) {
   constexpr int ITER = kStatsChunk / (kStatsThreads * VEC);
   __shared__ float sm[kStatsThreads / kWave], ss[kStatsThreads / kWave];
@@ -124,7 +129,7 @@ __global__ __launch_bounds__(kStatsThreads) void chain_stats_kernel(ChainArgs a)
     const int j = begin + (it * kStatsThreads + threadIdx.x) * VEC;
     if constexpr (VEC == 4) {
       float4 x = {kNegInf, kNegInf, kNegInf, kNegInf};
-      if (j < a.V) x = load_stream4(z + j);   // V % 4 == 0 on this path
+      if (j < a.V) x = load_stream4<NT>(z + j);   // V % 4 == 0 on this path
       v[it * 4 + 0] = x.x; v[it * 4 + 1] = x.y; v[it * 4 + 2] = x.z; v[it * 4 + 3] = x.w;
     } else {
       v[it] = j < a.V ? z[j] : kNegInf;
@@ -526,8 +531,10 @@ hipError_t launch_chain(const ChainPlan& p, const float* target, const float* dr
   const bool vec4 = (V % 4 == 0) && ((uintptr_t)target % 16 == 0) &&
                     (N == 0 || (uintptr_t)draft % 16 == 0);
   const dim3 g1(p.nchunks, B * p.rows_per_seq);
-  if (vec4) chain_stats_kernel<4><<<g1, kStatsThreads, 0, st>>>(a);
-  else chain_stats_kernel<1><<<g1, kStatsThreads, 0, st>>>(a);
+  const bool stream = (size_t)B * p.rows_per_seq * V * sizeof(float) > kCachedLogitBytes;
+  if (vec4 && stream) chain_stats_kernel<4, true><<<g1, kStatsThreads, 0, st>>>(a);
+  else if (vec4) chain_stats_kernel<4, false><<<g1, kStatsThreads, 0, st>>>(a);
+  else chain_stats_kernel<1, false><<<g1, kStatsThreads, 0, st>>>(a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int cpb = p.cpb == 1 ? 1 : vec4 ? kDrawCpbLarge : kDrawCpbScalar;
