@@ -93,8 +93,8 @@ const char* spec_status_string(spec_status status);
  *   scale    softmax scale, normally 1/sqrt(D); must be finite and > 0
  *
  * Limits: 1 <= T <= 64, D in {64, 128}, Hkv >= 1, Hq % Hkv == 0, ctx >= 0,
- * B·Hkv <= SPEC_MAX_ROWS; q, k, v and out 16-byte aligned (SPEC_ERR_UNSUPPORTED
- * otherwise).
+ * (ctx + T)·D < 2^31, B·Hkv <= SPEC_MAX_ROWS; q, k, v and out 16-byte aligned
+ * (SPEC_ERR_UNSUPPORTED otherwise).
  * ------------------------------------------------------------------------- */
 size_t spec_verify_attention_workspace(int B, int T, int Hq, int Hkv, int D, int ctx,
                                        spec_dtype dtype);
@@ -319,7 +319,8 @@ spec_status spec_ngram_propose(const int32_t* context, const int32_t* context_le
  *               num_accepted (clamped to [0, T-1] on the device)
  *   new_len     [B] int32 out
  *
- * Limits: 1 <= T <= 64, D in {64, 128}, Hkv >= 1, ctx >= 0.  No workspace.
+ * Limits: 1 <= T <= 64, D in {64, 128}, Hkv >= 1, ctx >= 0, (ctx + T)·D < 2^31.
+ * No workspace.
  * ------------------------------------------------------------------------- */
 spec_status spec_commit_kv(void* k, void* v, const int32_t* path, const int32_t* accept_len,
                            int32_t* new_len, int B, int T, int Hkv, int D, int ctx,
