@@ -32,6 +32,7 @@ if ROOT not in sys.path:
 
 METRIC = ("verify-step µs + achieved HBM GB/s (attn, sampler) at N=4/8; α overhead")
 HBM_PEAK_GBPS = 8000.0
+BF16_MFMA_PEAK_TFLOPS = 2500.0      # dense bf16 matrix peak (no sparsity)
 WORKLOAD = "large_batch_chain"
 ATTN_SOURCE = os.path.join(ROOT, "verify_pass_rejection_amd", "csrc", "attention.hip")
 TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "attention_large_batch_chain_hbm_traffic.txt")
@@ -461,6 +462,7 @@ def main():
     if not args.no_cpu_baseline and w.kind == "chain":
         cpu = cpu_baseline(w, step)
 
+    attn_tflops = attention_flops(w) / (t["attn_ms"] * 1e-3) / 1e12
     line = {
         "metric": METRIC,
         "value": round(step_gbps, 2),
@@ -488,13 +490,17 @@ def main():
         "sampler_GBps": round(samp_gbps, 1),
         "attn_frac_hbm_peak": round(attn_gbps / HBM_PEAK_GBPS, 4),
         "sampler_frac_hbm_peak": round(samp_gbps / HBM_PEAK_GBPS, 4),
-        "attn_TFLOPs": round(attention_flops(w) / (t["attn_ms"] * 1e-3) / 1e12, 2),
+        "attn_TFLOPs": round(attn_tflops, 2),
+        "attn_frac_bf16_mfma_peak": (round(attn_tflops / BF16_MFMA_PEAK_TFLOPS, 4)
+                                     if w.dtype == "bf16" else None),
         **alphas,
         "roofline": {"bound": "hbm", "achieved": round(attn_gbps, 1), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(attn_gbps / HBM_PEAK_GBPS, 4),
                      "traffic": measured_traffic() if w.name == WORKLOAD else None,
-                     "kernel": "attn_mfma_kernel (spec_verify_attention: one launch, one "
-                               "split per (sequence, KV head))",
+                     "kernel": ("attn_mfma_kernel (spec_verify_attention: one launch, one "
+                                "split per (sequence, KV head))" if w.name == WORKLOAD else
+                                "spec_verify_attention call: attn_mfma_kernel, or attn_valu_kernel "
+                                "for fp32, plus attn_combine_kernel when the keys are split"),
                      "algorithmic_bytes_per_launch": ab},
         "cpu_baseline": cpu,
     }
