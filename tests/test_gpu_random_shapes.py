@@ -8,7 +8,8 @@ and are not multiples of 4, temperatures other than 1.  Attention is compared
 element by element with oracle.attention (max-abs 1e-4 fp32, 2e-2 bf16), and
 over a paged cache (ragged prefix lengths, page sizes 1-256, both layouts) with
 oracle.paged; chain acceptance exactly on every unflagged sequence (band 1e-6),
-greedy tree acceptance exactly.
+greedy tree acceptance exactly, sampled tree acceptance on random trees exactly
+on every unflagged sequence.
 """
 import numpy as np
 import pytest
@@ -167,3 +168,53 @@ def test_paged_attention_random_shapes(seed):
     say(w.name, f"max_abs_err={err:.3e} tol={tol}")
     assert np.all(np.isfinite(got))
     assert err <= tol
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_sampled_tree_acceptance_random_trees(seed):
+    """Sampled tree acceptance on random trees (parent uniform over the earlier
+    nodes), random sizes, vocabularies and temperatures; every node's token is
+    drawn from its parent's draft distribution (Gumbel-max over the draft logits
+    divided by the temperature), so siblings may repeat a token.  Long walks
+    through many rejections are flagged more often than on the reference tree
+    shapes (up to a third of the sequences here); the unflagged ones, at least
+    half, must match the oracle exactly."""
+    from oracle.accept import tree_accept_sampled
+    dev = device()
+    g = torch.Generator().manual_seed(7000 + seed)
+    B = int(torch.randint(1, 17, (1,), generator=g))
+    T = int(torch.randint(1, 65, (1,), generator=g))
+    V = [5, 999, 4096, 32000, 40001, 2][seed]
+    tau = [1.0, 0.7, 1.3, 1.0, 2.0, 1.0][seed]
+    par = random_parents(B, T, g)
+    target = torch.randn((B, T, V), generator=g) * 2.0
+    draft = target + torch.randn((B, T, V), generator=g) * [1.0, 0.5, 1.0, 2.0, 1.0, 1.0][seed]
+    gumbel = -torch.log(-torch.log(torch.rand((B, T, V), generator=g).clamp_(1e-12, 1 - 1e-7)))
+    pidx = par.clamp(min=0).long()                  # node 0's token is never read
+    parent_rows = torch.gather(draft, 1, pidx[:, :, None].expand(B, T, V))
+    tokens = torch.argmax(parent_rows / tau + gumbel, dim=2).to(torch.int32)
+    u = lambda: ((torch.randint(1, 1 << 24, (B, T), generator=g).double()   # noqa: E731
+                  / float(1 << 24)).float())
+    ua, ud = u(), u()
+    al, path, out = nat.spec_accept_tree_sampled(target.to(dev), draft.to(dev), tokens.to(dev),
+                                                 par.to(dev), ua.to(dev), ud.to(dev),
+                                                 temperature=tau)
+    torch.cuda.synchronize()
+    ref = tree_accept_sampled(target.double().numpy(), draft.double().numpy(),
+                              tokens.numpy().astype(np.int64), par.numpy().astype(np.int64),
+                              ua.double().numpy(), ud.double().numpy(), temperature=tau,
+                              band=1e-6)
+    al, path, out = i64(al), i64(path), i64(out)
+    ok = ~ref.near_boundary
+    mism = ok & ((al != ref.accept_len) | np.any(path != ref.path, axis=1)
+                 | np.any(out != ref.out_tokens, axis=1))
+    say(f"sampled tree seed {seed}", f"B={B} T={T} V={V} tau={tau}",
+        f"flagged={int((~ok).sum())} mismatched={int(mism.sum())} mean_accepted={al.mean():.2f}")
+    assert not mism.any(), np.nonzero(mism)[0][:10]
+    assert ok.sum() * 2 >= B
+    for b in range(B):                     # every sequence, flagged or not, is well formed
+        n = al[b]
+        assert 0 <= n < T and path[b, 0] == 0 and np.all(path[b, n + 1:] == -1)
+        assert all(par[b, path[b, i + 1]] == path[b, i] for i in range(n))
+        assert 0 <= out[b, n] < V and np.all(out[b, n + 1:] == -1)
+        assert np.array_equal(out[b, :n], tokens[b, path[b, 1:n + 1]].numpy())
