@@ -9,7 +9,8 @@ element by element with oracle.attention (max-abs 1e-4 fp32, 2e-2 bf16), and
 over a paged cache (ragged prefix lengths, page sizes 1-256, both layouts) with
 oracle.paged; chain acceptance exactly on every unflagged sequence (band 1e-6),
 greedy tree acceptance exactly, sampled tree acceptance on random trees exactly
-on every unflagged sequence.
+on every unflagged sequence; the KV commit of random root paths and n-gram
+drafting on random histories bit for bit.
 """
 import numpy as np
 import pytest
@@ -218,3 +219,57 @@ def test_sampled_tree_acceptance_random_trees(seed):
         assert all(par[b, path[b, i + 1]] == path[b, i] for i in range(n))
         assert 0 <= out[b, n] < V and np.all(out[b, n + 1:] == -1)
         assert np.array_equal(out[b, :n], tokens[b, path[b, 1:n + 1]].numpy())
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_kv_commit_random_paths(seed):
+    """The KV commit of a random root path (a random node and its ancestors) of
+    a random tree, bit for bit against oracle.commit: random batch, KV heads,
+    head dimension, prefix length, fp32 or bf16."""
+    from oracle.commit import commit_kv
+    dev = device()
+    c = attention_case(300 + seed)
+    g = c["g"]
+    w = I.WORKLOADS["large_batch_chain"].with_(
+        name=f"commit_random_{seed}", B=c["B"], T=c["T"], Hq=c["Hkv"], Hkv=c["Hkv"], D=c["D"],
+        ctx=c["ctx"], dtype=c["dtype"], seed=800 + seed)
+    _, k, v = I.make_attention_inputs(w, dev)
+    par = random_parents(w.B, w.T, g)
+    acc = torch.zeros(w.B, dtype=torch.int32)
+    path = torch.full((w.B, w.T), -1, dtype=torch.int32)
+    for b in range(w.B):
+        n = int(torch.randint(0, w.T, (1,), generator=g))
+        nodes = [n]
+        while nodes[-1] != 0:
+            nodes.append(int(par[b, nodes[-1]]))
+        nodes.reverse()
+        acc[b] = len(nodes) - 1
+        path[b, :len(nodes)] = torch.tensor(nodes, dtype=torch.int32)
+    host = (lambda t: t.view(torch.int16).cpu().numpy() if t.dtype == torch.bfloat16  # noqa: E731
+            else t.cpu().numpy())
+    want_k, want_v, want_n = commit_kv(host(k), host(v), w.ctx, acc.numpy(), path.numpy())
+    say(w.name, f"B={w.B} T={w.T} Hkv={w.Hkv} D={w.D} ctx={w.ctx} {w.dtype}",
+        f"accept_len={acc.tolist()}")
+    n = nat.spec_commit_kv(k, v, w.ctx, acc.to(dev), path=path.to(dev))
+    torch.cuda.synchronize()
+    assert np.array_equal(n.cpu().numpy(), want_n)
+    assert np.array_equal(host(k), want_k)
+    assert np.array_equal(host(v), want_v)
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_ngram_random_histories(seed):
+    """n-gram drafting on seeded random histories: batch, length (ragged per
+    sequence), vocabulary, number of drafts and n-gram range all drawn."""
+    from test_gpu_ngram import compare
+    dev = device()
+    g = torch.Generator().manual_seed(9000 + seed)
+    B = int(torch.randint(1, 33, (1,), generator=g))
+    L = int(torch.randint(1, 12000, (1,), generator=g))
+    V = [2, 5, 50, 1000, 32000, 3][seed]
+    N = int(torch.randint(0, 64, (1,), generator=g))
+    n_min = int(torch.randint(1, 5, (1,), generator=g))
+    n_max = n_min + int(torch.randint(0, 6, (1,), generator=g))
+    w = I.WORKLOADS["large_batch_chain"].with_(B=B, ctx=L, V=V, seed=950 + seed)
+    ctx, lens = I.make_ngram_inputs(w, dev)
+    compare(ctx, lens, N, n_min, n_max, label=f"ngram seed {seed} V={V}")
