@@ -107,3 +107,21 @@ def test_tree_planting_rate():
             total += 1
             hits += int(z[b, p, int(tok[b, i])] == I.PLANT_SIGMAS * w.target_sd)
     assert 0.6 < hits / total < 0.95
+
+
+def test_tree_inputs_with_one_and_two_token_vocabularies():
+    # one token: no sibling can avoid the planted token, so every token is 0 and
+    # the generator still ends; two tokens: a planted node's other children get
+    # the other token
+    w1 = small("eagle2_tree", V=1, B=2)
+    d1 = I.make_tree_inputs(w1)
+    assert d1["tokens"].shape == (2, w1.T) and bool((d1["tokens"] == 0).all())
+    w2 = small("medusa70b_tree", V=2, B=3)
+    d2 = I.make_tree_inputs(w2)
+    par, tok = d2["parents"], d2["tokens"]
+    for b in range(w2.B):
+        kids = {}
+        for i in range(1, w2.T):
+            kids.setdefault(int(par[b, i]), []).append(i)
+        for ch in kids.values():
+            assert all(int(tok[b, c]) != int(tok[b, ch[0]]) for c in ch[1:])
