@@ -269,4 +269,6 @@ def test_commit_validation():
     assert commit(ctx=(1 << 31) - 2) == UNSUP      # ctx + T past int32, no overflow
     assert commit(dtype=3) == UNSUP
     assert commit(v=FAKE + 8) == UNSUP         # 16-byte vectors
+    assert commit(B=1 << 29, Hkv=8) == UNSUP   # B*Hkv past int32 block ids
+    assert commit(B=(1 << 28) - 1, Hkv=8, acc=None) == NULL
     assert commit(B=0, acc=None) == OK         # empty problem: nothing launched

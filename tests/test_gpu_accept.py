@@ -180,3 +180,23 @@ def test_chain_fallbacks_across_draw_chunks():
     num, out, _ = compare_chain(d, label="chunked fallbacks")
     assert np.all(num[0:16] == 0)
     assert np.all(out[16:32][np.arange(16), num[16:32]] == 17000)
+
+
+def test_chain_on_a_side_stream():
+    """The call on a stream other than the current one, with the workspace and
+    outputs allocated by the binding: allocations made on the current stream
+    right after the call must not take their memory while the kernels run."""
+    dev = device()
+    d = I.make_chain_inputs(I.WORKLOADS["llama3_8b_chain"].with_(B=16, seed=57), dev)
+    args = (d["target_logits"], d["draft_logits"], d["draft_tokens"], d["u_accept"],
+            d["u_draw"])
+    want = nat.spec_accept_chain(*args)
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    got = [nat.spec_accept_chain(*args, stream=side) for _ in range(4)]
+    junk = [torch.full((1 << 20,), -7, dtype=torch.int32, device=dev) for _ in range(8)]
+    torch.cuda.synchronize()
+    del junk
+    for num, out in got:
+        assert torch.equal(num, want[0]) and torch.equal(out, want[1])

@@ -131,3 +131,35 @@ def test_law_chi2_on_gpu():
         chi = stats.chisquare(np.bincount(out[sel, 1], minlength=V), sel.sum() * p[a]).statistic
         say(f"chi2(token after node {a} vs p_{a}) = {chi:.2f} over {int(sel.sum())} trials")
         assert chi < crit
+
+
+def test_masked_vocabulary_chunks():
+    """Top-k style masking: on both the target and the draft rows every logit
+    outside a per-sequence allowed set is -inf, and whole 8192-logit chunks of
+    the 32000-token vocabulary hold nothing else (their maximum is -inf and
+    they carry no mass).  Node tokens are re-drawn from the parent's masked
+    draft row, so every draft lies in the allowed set."""
+    dev = device()
+    w = I.WORKLOADS["eagle2_tree"].with_(B=6, V=32000, seed=47)
+    d = I.make_sampled_tree_inputs(w, dev)
+    g = torch.Generator(device=dev).manual_seed(4701)
+    B, T, V = w.B, w.T, w.V
+    allowed = torch.zeros((B, V), dtype=torch.bool, device=dev)
+    allowed[:, :8192] = torch.rand((B, 8192), generator=g, device=dev) < 0.05   # chunk 0
+    allowed[:, 24576:] = torch.rand((B, V - 24576), generator=g, device=dev) < 0.02  # chunk 3
+    allowed[1, :8192] = False             # sequence 1: chunks 0-2 empty
+    allowed[2, 24576:] = False            # sequence 2: chunks 1-3 empty
+    allowed[:, 0] |= ~allowed.any(dim=1)
+    mask = (~allowed)[:, None, :].expand(B, T, V)
+    tgt = d["target_logits"].masked_fill(mask, -float("inf"))
+    drf = d["draft_logits"].masked_fill(mask, -float("inf"))
+    par = d["parents"].long().clamp(min=0)
+    gu = I.uniforms((B, T, V), g, dev).double()
+    rows = torch.gather(drf, 1, par[:, :, None].expand(B, T, V)).double()
+    tok = torch.argmax(rows - torch.log(-torch.log(gu)), dim=-1).to(torch.int32)
+    tok[:, 0] = 0
+    dm = dict(d, target_logits=tgt.contiguous(), draft_logits=drf.contiguous(), tokens=tok)
+    al, path, out = compare(dm, label="masked chunks")
+    for b in range(B):
+        n = al[b]
+        assert bool(allowed[b, int(out[b, n])])       # the drawn token has mass

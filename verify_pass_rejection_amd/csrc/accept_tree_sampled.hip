@@ -167,11 +167,15 @@ __global__ __launch_bounds__(kSTThreads) void stree_stats_kernel(STreeArgs a) {
   for (int i = 1; i < PER; ++i) mx = fmaxf(mx, x[i]);
   mx = block_max(mx, redf);
   double s = 0.0;
-  // groups of four terms in float32 (at most 3 roundings), groups in float64
+  // groups of four terms in float32 (at most 3 roundings), groups in float64;
+  // a chunk of -inf logits (a masked vocabulary range) has no mass: its
+  // maximum stays -inf and its sum 0, which the walk's merge weighs 0
+  if (mx != -__builtin_huge_valf()) {
 #pragma unroll
-  for (int i = 0; i < PER; i += 4)
-    s += (double)((e_bulk(x[i], mx, a.k2f) + e_bulk(x[i + 1], mx, a.k2f)) +
-                  (e_bulk(x[i + 2], mx, a.k2f) + e_bulk(x[i + 3], mx, a.k2f)));
+    for (int i = 0; i < PER; i += 4)
+      s += (double)((e_bulk(x[i], mx, a.k2f) + e_bulk(x[i + 1], mx, a.k2f)) +
+                    (e_bulk(x[i + 2], mx, a.k2f) + e_bulk(x[i + 3], mx, a.k2f)));
+  }
   s = block_sum(s, red);
   if (threadIdx.x == 0) {
     const size_t o = ((size_t)kind * a.B * a.T + row) * a.nchunks + ch;

@@ -256,6 +256,7 @@ spec_status spec_commit_kv(void* k, void* v, const int32_t* path, const int32_t*
   if (dtype != SPEC_F32 && dtype != SPEC_BF16) return SPEC_ERR_UNSUPPORTED;
   if (T > SPEC_MAX_T || (D != 64 && D != 128)) return SPEC_ERR_UNSUPPORTED;
   if (((long long)ctx + T) * D >= (1ll << 31)) return SPEC_ERR_UNSUPPORTED;
+  if ((long long)B * Hkv > SPEC_MAX_ROWS) return SPEC_ERR_UNSUPPORTED;   // int32 block ids
   if (B == 0) return SPEC_OK;
   if (!accept_len || !new_len) return SPEC_ERR_NULL;
   if (path != nullptr) {

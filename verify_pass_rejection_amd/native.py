@@ -3,8 +3,11 @@
 Argument marshalling only: tensors are checked for device, dtype, shape and
 contiguity, their device pointers and the current HIP stream are passed to the
 library, and a non-OK status raises.  Every step of the computation runs in
-the library's HIP kernels; there is no fallback.  Workspaces are allocated
-with torch when the caller does not pass one.
+the library's HIP kernels; there is no fallback.  Workspaces (and outputs the
+caller does not pass) are allocated with torch on the current stream; when
+the call runs on another stream (``stream=``), that stream is recorded on
+them, so the caching allocator does not reuse their memory before the
+kernels are done.
 """
 from __future__ import annotations
 
@@ -100,6 +103,21 @@ def _stream(stream) -> int | None:
     return stream.cuda_stream
 
 
+def _keep_for_stream(stream, *tensors):
+    """Tensors the binding allocated (workspaces, outputs) come from torch's
+    caching allocator on the current stream.  When the kernels run on another
+    stream, that stream is recorded on each tensor, so that its memory is not
+    handed to another tensor before the kernels that use it have finished."""
+    if stream is None:
+        return
+    s = torch.cuda.ExternalStream(stream) if isinstance(stream, int) else stream
+    if s.cuda_stream == torch.cuda.current_stream().cuda_stream:
+        return
+    for t in tensors:
+        if t is not None:
+            t.record_stream(s)
+
+
 def _check(t, name, shape, dtype, device):
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a torch.Tensor")
@@ -141,6 +159,7 @@ def spec_verify_attention(q, k, v, ctx, parents=None, out=None, scale=None,
     _check(q, "q", (B, T, Hq, D), q.dtype, dev)
     if parents is not None:
         _check(parents, "parents", (B, T), torch.int32, dev)
+    made_out = out is None
     if out is None:
         out = torch.empty((B, T, Hq, D), dtype=torch.float32, device=dev)
     _check(out, "out", (B, T, Hq, D), torch.float32, dev)
@@ -152,6 +171,7 @@ def spec_verify_attention(q, k, v, ctx, parents=None, out=None, scale=None,
                                       B, T, Hq, Hkv, D, ctx, dt, float(scale),
                                       _ptr(ws), ws.numel() * ws.element_size(), _stream(stream))
     _raise(st, "spec_verify_attention")
+    _keep_for_stream(stream, ws if workspace is None else None, out if made_out else None)
     return out
 
 
@@ -191,6 +211,7 @@ def spec_verify_attention_paged(q, k_pages, v_pages, block_table, max_ctx, ctx_l
         _check(ctx_lens, "ctx_lens", (B,), torch.int32, dev)
     if parents is not None:
         _check(parents, "parents", (B, T), torch.int32, dev)
+    made_out = out is None
     if out is None:
         out = torch.empty((B, T, Hq, D), dtype=torch.float32, device=dev)
     _check(out, "out", (B, T, Hq, D), torch.float32, dev)
@@ -203,6 +224,7 @@ def spec_verify_attention_paged(q, k_pages, v_pages, block_table, max_ctx, ctx_l
         _ptr(out), B, T, Hq, Hkv, D, max_ctx, ps, P, block_table.shape[1], _LAYOUTS[layout], dt,
         float(scale), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream))
     _raise(st, "spec_verify_attention_paged")
+    _keep_for_stream(stream, ws if workspace is None else None, out if made_out else None)
     return out
 
 
@@ -223,6 +245,7 @@ def spec_accept_chain(target_logits, draft_logits, draft_tokens, u_accept, u_dra
     _check(draft_tokens, "draft_tokens", (B, N), torch.int32, dev)
     _check(u_accept, "u_accept", (B, N), torch.float32, dev)
     _check(u_draw, "u_draw", (B, N + 1), torch.float32, dev)
+    made = [num_accepted is None, out_tokens is None]
     if num_accepted is None:
         num_accepted = torch.empty(B, dtype=torch.int32, device=dev)
     if out_tokens is None:
@@ -235,6 +258,8 @@ def spec_accept_chain(target_logits, draft_logits, draft_tokens, u_accept, u_dra
                                   _ptr(num_accepted), _ptr(out_tokens), B, N, V,
                                   _ptr(ws), ws.numel() * ws.element_size(), _stream(stream))
     _raise(st, "spec_accept_chain")
+    _keep_for_stream(stream, ws if workspace is None else None,
+                     num_accepted if made[0] else None, out_tokens if made[1] else None)
     return num_accepted, out_tokens
 
 
@@ -251,6 +276,7 @@ def spec_accept_tree(target_logits, tokens, parents, accept_len=None, path=None,
     _check(target_logits, "target_logits", (B, T, V), torch.float32, dev)
     _check(tokens, "tokens", (B, T), torch.int32, dev)
     _check(parents, "parents", (B, T), torch.int32, dev)
+    made = [accept_len is None, path is None, out_tokens is None]
     if accept_len is None:
         accept_len = torch.empty(B, dtype=torch.int32, device=dev)
     if path is None:
@@ -262,6 +288,8 @@ def spec_accept_tree(target_logits, tokens, parents, accept_len=None, path=None,
                                  _ptr(accept_len), _ptr(path), _ptr(out_tokens), B, T, V,
                                  _ptr(ws), ws.numel() * ws.element_size(), _stream(stream))
     _raise(st, "spec_accept_tree")
+    _keep_for_stream(stream, ws if workspace is None else None,
+                     *(t for t, m in zip((accept_len, path, out_tokens), made) if m))
     return accept_len, path, out_tokens
 
 
@@ -281,6 +309,7 @@ def spec_accept_tree_sampled(target_logits, draft_logits, tokens, parents, u_acc
     _check(parents, "parents", (B, T), torch.int32, dev)
     _check(u_accept, "u_accept", (B, T), torch.float32, dev)
     _check(u_draw, "u_draw", (B, T), torch.float32, dev)
+    made = [accept_len is None, path is None, out_tokens is None]
     if accept_len is None:
         accept_len = torch.empty(B, dtype=torch.int32, device=dev)
     if path is None:
@@ -293,6 +322,8 @@ def spec_accept_tree_sampled(target_logits, draft_logits, tokens, parents, u_acc
         _ptr(u_draw), float(temperature), _ptr(accept_len), _ptr(path), _ptr(out_tokens),
         B, T, V, _ptr(ws), ws.numel() * ws.element_size(), _stream(stream))
     _raise(st, "spec_accept_tree_sampled")
+    _keep_for_stream(stream, ws if workspace is None else None,
+                     *(t for t, m in zip((accept_len, path, out_tokens), made) if m))
     return accept_len, path, out_tokens
 
 
@@ -308,6 +339,7 @@ def spec_ngram_propose(context, N, n_min=1, n_max=4, context_lens=None, num_draf
     _check(context, "context", (B, L), torch.int32, dev)
     if context_lens is not None:
         _check(context_lens, "context_lens", (B,), torch.int32, dev)
+    made = [num_drafts is None, drafts is None]
     if num_drafts is None:
         num_drafts = torch.empty(B, dtype=torch.int32, device=dev)
     if drafts is None:
@@ -318,6 +350,8 @@ def spec_ngram_propose(context, N, n_min=1, n_max=4, context_lens=None, num_draf
                                    _ptr(drafts), B, L, N, n_min, n_max, _ptr(ws),
                                    ws.numel() * ws.element_size(), _stream(stream))
     _raise(st, "spec_ngram_propose")
+    _keep_for_stream(stream, ws if workspace is None else None,
+                     num_drafts if made[0] else None, drafts if made[1] else None)
     return num_drafts, drafts
 
 
@@ -332,9 +366,11 @@ def spec_commit_kv(k, v, ctx, accept_len, path=None, new_len=None, stream=None):
     _check(accept_len, "accept_len", (B,), torch.int32, dev)
     if path is not None:
         _check(path, "path", (B, T), torch.int32, dev)
+    made = new_len is None
     if new_len is None:
         new_len = torch.empty(B, dtype=torch.int32, device=dev)
     st = load().spec_commit_kv(_ptr(k), _ptr(v), _ptr(path), _ptr(accept_len), _ptr(new_len),
                                B, T, Hkv, D, ctx, dt, _stream(stream))
     _raise(st, "spec_commit_kv")
+    _keep_for_stream(stream, new_len if made else None)
     return new_len
