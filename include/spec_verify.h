@@ -19,10 +19,12 @@
  * Conventions shared by every entry point
  * ---------------------------------------
  *  - Every data pointer is a caller-owned DEVICE buffer, dense row-major in the
- *    layout stated at each argument.  The library keeps no state and allocates
- *    no memory; scratch space comes from the caller's `workspace` (device
- *    memory, at least the size the matching *_workspace() query returns, no
- *    alignment beyond 256 bytes required, contents need not be initialised).
+ *    layout stated at each argument.  The library allocates no memory; scratch
+ *    space comes from the caller's `workspace` (device memory, at least the
+ *    size the matching *_workspace() query returns, no alignment beyond 256
+ *    bytes required, contents need not be initialised).  The one exception is
+ *    spec_accept_chain_noalloc, whose scratch is a static device array of the
+ *    library; no other call keeps state between calls.
  *  - Work is enqueued asynchronously on `hip_stream` (a hipStream_t; NULL means
  *    the null stream).  Outputs are valid once that stream reaches the point
  *    after the call.  Concurrent calls must use distinct workspaces.
@@ -191,6 +193,31 @@ spec_status spec_accept_chain(const float* target_logits, const float* draft_log
                               int32_t* num_accepted, int32_t* out_tokens,
                               int B, int N, int V,
                               void* workspace, size_t workspace_bytes, void* hip_stream);
+
+/* ---------------------------------------------------------------------------
+ * Chain acceptance without a workspace, for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc.
+ *
+ * Arguments, results and errors are spec_accept_chain's, computed by the same
+ * kernels.  The scratch they need (what spec_accept_chain_workspace sizes) is
+ * a static device array of the library, SPEC_CHAIN_NOALLOC_SCRATCH_BYTES on
+ * every GPU it runs on, held until the process ends; its address is looked up
+ * once per device, at the first call there.  The call allocates nothing.
+ * Problems that need more scratch (spec_accept_chain_workspace(B, N, V) >
+ * SPEC_CHAIN_NOALLOC_SCRATCH_BYTES; for example B = 1024, N = 8, V = 152064
+ * needs 1.6 MB) return SPEC_ERR_WORKSPACE before anything is enqueued.
+ * Every call on one GPU uses the same array: calls ordered on one stream are
+ * safe, calls that may overlap on one GPU (several streams, several host
+ * threads) race and give unspecified results.
+ * ------------------------------------------------------------------------- */
+#define SPEC_CHAIN_NOALLOC_SCRATCH_BYTES ((size_t)4 << 20)
+
+spec_status spec_accept_chain_noalloc(const float* target_logits, const float* draft_logits,
+                                      const int32_t* draft_tokens, const float* u_accept,
+                                      const float* u_draw, float temperature,
+                                      int32_t* num_accepted, int32_t* out_tokens,
+                                      int B, int N, int V, void* hip_stream);
 
 /* ---------------------------------------------------------------------------
  * Greedy tree acceptance (glossary "L'attention en arbre : la brique commune";

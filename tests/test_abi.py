@@ -25,7 +25,7 @@ def declared_functions():
 def test_library_loads_and_exports_every_declared_symbol():
     lib = nat.load()
     decl = declared_functions()
-    assert len(decl) == 14
+    assert len(decl) == 15
     for name in decl:
         assert hasattr(lib, name), name
     assert sorted(nat.exported_symbols()) == decl
@@ -150,6 +150,37 @@ def test_chain_validation():
     assert chain(B=0, t=None) == OK
     # N = 0 needs no draft rows, tokens or accept uniforms
     assert chain(N=0, d=None, x=None, ua=None, ws_bytes=8) == WS
+
+
+def chain_noalloc(**kw):
+    a = dict(t=FAKE, d=FAKE, x=FAKE, ua=FAKE, ud=FAKE, tau=1.0, na=FAKE, out=FAKE,
+             B=4, N=3, V=1000, stream=None)
+    a.update(kw)
+    return nat.load().spec_accept_chain_noalloc(a["t"], a["d"], a["x"], a["ua"], a["ud"],
+                                                a["tau"], a["na"], a["out"], a["B"], a["N"],
+                                                a["V"], a["stream"])
+
+
+def test_chain_noalloc_validation():
+    """The same checks as spec_accept_chain, and problems whose workspace
+    would exceed the static scratch are refused before any HIP call."""
+    assert chain_noalloc(t=None) == NULL
+    assert chain_noalloc(d=None) == NULL
+    assert chain_noalloc(ud=None) == NULL
+    assert chain_noalloc(out=None) == NULL
+    assert chain_noalloc(tau=0.0) == SHAPE
+    assert chain_noalloc(V=0) == SHAPE
+    assert chain_noalloc(N=64) == UNSUP
+    assert chain_noalloc(B=1 << 29, N=3) == UNSUP
+    assert chain_noalloc(B=0, t=None) == OK
+    limit = nat.CHAIN_NOALLOC_SCRATCH_BYTES
+    assert nat.spec_accept_chain_workspace(64, 8, 152064) <= limit       # the large batch fits
+    assert nat.spec_accept_chain_workspace(1024, 8, 152064) <= limit
+    assert nat.spec_accept_chain_workspace(4096, 8, 152064) > limit
+    assert chain_noalloc(B=4096, N=8, V=152064) == WS
+    assert chain_noalloc(B=64, N=63, V=1 << 24) == WS
+    header = open(HEADER).read()
+    assert f"#define SPEC_CHAIN_NOALLOC_SCRATCH_BYTES ((size_t){limit >> 20} << 20)" in header
 
 
 def test_chain_workspace_sizes():

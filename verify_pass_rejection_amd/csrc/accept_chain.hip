@@ -26,6 +26,8 @@
 // and then taking the first rejection gives the same result as the
 // sequential walk.
 
+#include <mutex>
+
 #include "common.h"
 
 namespace sv {
@@ -551,6 +553,44 @@ hipError_t launch_chain(const ChainPlan& p, const float* target, const float* dr
   if (vec4) chain_select_kernel<4><<<B, kDrawThreads, 0, st>>>(a);
   else chain_select_kernel<1><<<B, kDrawThreads, 0, st>>>(a);
   return hipGetLastError();
+}
+
+// ---- scratch of the allocation-free entry point --------------------------------
+// spec_accept_chain_noalloc runs the kernels above with their workspace in
+// this array.  Each GPU the library runs on holds its own copy until the
+// process ends, and every call on that GPU shares it.  Nothing in it needs
+// clearing: every kernel writes what it later reads within one call.  Host
+// code never passes the array's name to a kernel (on the host it is only a
+// stand-in for the symbol); chain_scratch gives its device address.
+static __device__ __align__(256) unsigned char scratch[kChainScratchBytes];
+
+// The device address of the scratch array on the GPU that runs `st` (the
+// current device for the null stream), looked up once per device with that
+// device current and kept.
+hipError_t chain_scratch(hipStream_t st, void** ptr) {
+  static std::mutex mu;
+  static void* addr[kMaxScratchDevices] = {};
+  int dev = 0;
+  hipError_t e = st != nullptr ? hipStreamGetDevice(st, &dev) : hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxScratchDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (addr[dev] == nullptr) {
+    int cur = 0;
+    if ((e = hipGetDevice(&cur)) != hipSuccess) return e;
+    if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess) return e;
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (cur != dev) {
+      const hipError_t back = hipSetDevice(cur);
+      if (e == hipSuccess) e = back;
+    }
+    if (e != hipSuccess) return e;
+    if (p == nullptr) return hipErrorInvalidSymbol;
+    addr[dev] = p;
+  }
+  *ptr = addr[dev];
+  return hipSuccess;
 }
 
 }  // namespace sv

@@ -88,4 +88,9 @@ struct PagedKV {
 
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
+// Size of the static scratch array of the allocation-free chain acceptance
+// (one per GPU; it holds the workspace spec_accept_chain would take).
+constexpr size_t kChainScratchBytes = size_t(4) << 20;
+constexpr int kMaxScratchDevices = 64;
+
 }  // namespace sv

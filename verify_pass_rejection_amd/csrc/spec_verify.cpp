@@ -18,6 +18,7 @@ hipError_t launch_chain(const ChainPlan& p, const float* target, const float* dr
                         const int32_t* tokens, const float* u_acc, const float* u_draw,
                         float temperature, int32_t* num_acc, int32_t* out, int B, int N, int V,
                         void* workspace, hipStream_t st);
+hipError_t chain_scratch(hipStream_t st, void** ptr);
 TreePlan plan_tree(int B, int T, int V);
 hipError_t launch_tree(const TreePlan& p, const float* logits, const int32_t* tokens,
                        const int32_t* parents, int32_t* accept_len, int32_t* path,
@@ -56,6 +57,24 @@ spec_status check_chain(int B, int N, int V) {
   if ((long long)B * (2 * N + 1) > SPEC_MAX_ROWS) return SPEC_ERR_UNSUPPORTED;
   return SPEC_OK;
 }
+
+// Everything spec_accept_chain checks except the workspace.
+spec_status check_chain_call(const float* target_logits, const float* draft_logits,
+                             const int32_t* draft_tokens, const float* u_accept,
+                             const float* u_draw, float temperature,
+                             const int32_t* num_accepted, const int32_t* out_tokens, int B,
+                             int N, int V) {
+  const spec_status c = check_chain(B, N, V);
+  if (c != SPEC_OK) return c;
+  if (!(temperature > 0.f) || !isfinite(temperature)) return SPEC_ERR_SHAPE;
+  if (B == 0) return SPEC_OK;
+  if (!target_logits || !u_draw || !num_accepted || !out_tokens) return SPEC_ERR_NULL;
+  if (N > 0 && (!draft_logits || !draft_tokens || !u_accept)) return SPEC_ERR_NULL;
+  return SPEC_OK;
+}
+
+static_assert(sv::kChainScratchBytes == SPEC_CHAIN_NOALLOC_SCRATCH_BYTES,
+              "the header states the scratch size");
 
 spec_status check_ngram(int B, int L, int N, int n_min, int n_max) {
   if (B < 0 || L < 0 || N < 0 || n_min < 1 || n_max < n_min) return SPEC_ERR_SHAPE;
@@ -162,18 +181,33 @@ spec_status spec_accept_chain(const float* target_logits, const float* draft_log
                               const float* u_draw, float temperature, int32_t* num_accepted,
                               int32_t* out_tokens, int B, int N, int V, void* workspace,
                               size_t workspace_bytes, void* hip_stream) {
-  const spec_status c = check_chain(B, N, V);
-  if (c != SPEC_OK) return c;
-  if (!(temperature > 0.f) || !isfinite(temperature)) return SPEC_ERR_SHAPE;
-  if (B == 0) return SPEC_OK;
-  if (!target_logits || !u_draw || !num_accepted || !out_tokens || !workspace)
-    return SPEC_ERR_NULL;
-  if (N > 0 && (!draft_logits || !draft_tokens || !u_accept)) return SPEC_ERR_NULL;
+  const spec_status c = check_chain_call(target_logits, draft_logits, draft_tokens, u_accept,
+                                         u_draw, temperature, num_accepted, out_tokens, B, N, V);
+  if (c != SPEC_OK || B == 0) return c;
+  if (!workspace) return SPEC_ERR_NULL;
   const sv::ChainPlan p = sv::plan_chain(B, N, V);
   if (workspace_bytes < p.total_bytes) return SPEC_ERR_WORKSPACE;
   const hipError_t e = sv::launch_chain(p, target_logits, draft_logits, draft_tokens, u_accept,
                                         u_draw, temperature, num_accepted, out_tokens, B, N, V,
                                         workspace, (hipStream_t)hip_stream);
+  return e == hipSuccess ? SPEC_OK : SPEC_ERR_HIP;
+}
+
+spec_status spec_accept_chain_noalloc(const float* target_logits, const float* draft_logits,
+                                      const int32_t* draft_tokens, const float* u_accept,
+                                      const float* u_draw, float temperature,
+                                      int32_t* num_accepted, int32_t* out_tokens, int B, int N,
+                                      int V, void* hip_stream) {
+  const spec_status c = check_chain_call(target_logits, draft_logits, draft_tokens, u_accept,
+                                         u_draw, temperature, num_accepted, out_tokens, B, N, V);
+  if (c != SPEC_OK || B == 0) return c;
+  const sv::ChainPlan p = sv::plan_chain(B, N, V);
+  if (p.total_bytes > SPEC_CHAIN_NOALLOC_SCRATCH_BYTES) return SPEC_ERR_WORKSPACE;
+  void* scratch = nullptr;
+  if (sv::chain_scratch((hipStream_t)hip_stream, &scratch) != hipSuccess) return SPEC_ERR_HIP;
+  const hipError_t e = sv::launch_chain(p, target_logits, draft_logits, draft_tokens, u_accept,
+                                        u_draw, temperature, num_accepted, out_tokens, B, N, V,
+                                        scratch, (hipStream_t)hip_stream);
   return e == hipSuccess ? SPEC_OK : SPEC_ERR_HIP;
 }
 

@@ -38,6 +38,8 @@ _SIGNATURES = {
     "spec_accept_chain_workspace": (_c.c_size_t, [_c.c_int] * 3),
     "spec_accept_chain": (_c.c_int, [_c.c_void_p] * 5 + [_c.c_float] + [_c.c_void_p] * 2
                           + [_c.c_int] * 3 + [_c.c_void_p, _c.c_size_t, _c.c_void_p]),
+    "spec_accept_chain_noalloc": (_c.c_int, [_c.c_void_p] * 5 + [_c.c_float] + [_c.c_void_p] * 2
+                                  + [_c.c_int] * 3 + [_c.c_void_p]),
     "spec_accept_tree_workspace": (_c.c_size_t, [_c.c_int] * 3),
     "spec_accept_tree": (_c.c_int, [_c.c_void_p] * 6 + [_c.c_int] * 3
                          + [_c.c_void_p, _c.c_size_t, _c.c_void_p]),
@@ -260,6 +262,32 @@ def spec_accept_chain(target_logits, draft_logits, draft_tokens, u_accept, u_dra
     _raise(st, "spec_accept_chain")
     _keep_for_stream(stream, ws if workspace is None else None,
                      num_accepted if made[0] else None, out_tokens if made[1] else None)
+    return num_accepted, out_tokens
+
+
+#: Scratch of spec_accept_chain_noalloc per GPU (SPEC_CHAIN_NOALLOC_SCRATCH_BYTES).
+CHAIN_NOALLOC_SCRATCH_BYTES = 4 << 20
+
+
+def spec_accept_chain_noalloc(target_logits, draft_logits, draft_tokens, u_accept, u_draw,
+                              num_accepted, out_tokens, temperature=1.0, stream=None):
+    """spec_accept_chain with the library's static scratch instead of a
+    workspace: the caller passes the outputs and nothing is allocated."""
+    B, N1, V = target_logits.shape
+    N = N1 - 1
+    dev = target_logits.device
+    _check(target_logits, "target_logits", (B, N + 1, V), torch.float32, dev)
+    _check(draft_logits, "draft_logits", (B, N, V), torch.float32, dev)
+    _check(draft_tokens, "draft_tokens", (B, N), torch.int32, dev)
+    _check(u_accept, "u_accept", (B, N), torch.float32, dev)
+    _check(u_draw, "u_draw", (B, N + 1), torch.float32, dev)
+    _check(num_accepted, "num_accepted", (B,), torch.int32, dev)
+    _check(out_tokens, "out_tokens", (B, N + 1), torch.int32, dev)
+    st = load().spec_accept_chain_noalloc(_ptr(target_logits), _ptr(draft_logits),
+                                          _ptr(draft_tokens), _ptr(u_accept), _ptr(u_draw),
+                                          float(temperature), _ptr(num_accepted),
+                                          _ptr(out_tokens), B, N, V, _stream(stream))
+    _raise(st, "spec_accept_chain_noalloc")
     return num_accepted, out_tokens
 
 
