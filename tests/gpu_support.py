@@ -9,6 +9,26 @@ from verify_pass_rejection_amd import native as nat
 
 BF16_ATOL = 2e-2      # max-abs tolerance for bf16 K/V attention outputs
 F32_ATOL = 1e-4       # max-abs tolerance for fp32 attention outputs
+# Relative to the reference's own spread: an attention output over L keys has
+# an rms of about sqrt(1/L) (1e-2 at 8192 keys), so the max-abs contracts alone
+# would pass a mis-normalised result at long prefixes; the largest error must
+# also stay within this fraction of rms(reference).
+BF16_REL = 0.1
+F32_REL = 1e-3
+
+
+def assert_attention_close(got, want, dtype, label="", atol=None):
+    """Attention output against the oracle: finite, max-abs within the
+    contract (2e-2 bf16, 1e-4 fp32) and within BF16_REL / F32_REL of the
+    reference's rms."""
+    tol = atol if atol is not None else (F32_ATOL if dtype == "f32" else BF16_ATOL)
+    rel = F32_REL if dtype == "f32" else BF16_REL
+    err = float(np.max(np.abs(got - want)))
+    rms = float(np.sqrt(np.mean(np.square(want))))
+    say(label, f"max_abs_err={err:.3e} tol={tol} rms(ref)={rms:.3e} err/rms={err / rms:.2e}")
+    assert np.all(np.isfinite(got))
+    assert err <= tol
+    assert err <= rel * rms
 
 
 def device():
@@ -30,3 +50,60 @@ def f64(t):
 
 def i64(t):
     return t.detach().to("cpu").to(torch.int64).numpy()
+
+
+#: Relative margin beyond each decision's own error bound inside which the
+#: acceptance tests treat it as flagged (the verification allows up to 1e-5).
+TEST_BAND = 1e-6
+
+
+def check_chain(d, num, out, temperature=1.0, band=TEST_BAND, label=""):
+    """Every sequence of a chain acceptance against the oracle: one whose
+    decisions are all unflagged must match it exactly; a flagged one must
+    match one of its admissible outcomes (the oracle rerun with each flagged
+    uniform moved to either side of its boundary).  No test input may leave
+    a residual within its error of empty.  Returns the oracle's result."""
+    from oracle.accept import chain_accept, chain_admissible
+    args = (f64(d["target_logits"]), f64(d["draft_logits"]), i64(d["draft_tokens"]),
+            f64(d["u_accept"]), f64(d["u_draw"]))
+    ref = chain_accept(*args, temperature=temperature, band=band)
+    num, out = i64(num), i64(out)
+    ok = ~ref.near_boundary
+    mism = ok & ((num != ref.num_accepted) | np.any(out != ref.out_tokens, axis=1))
+    assert not mism.any(), np.nonzero(mism)[0][:10]
+    assert not ref.empty_ambiguous.any(), np.nonzero(ref.empty_ambiguous)[0]
+    n_alt = 0
+    for b in np.flatnonzero(~ok):
+        alts = chain_admissible(*args, b, temperature=temperature, band=band)
+        got = (int(num[b]), tuple(int(t) for t in out[b]))
+        assert got in alts, (b, got, sorted(alts), ref.flags[b])
+        n_alt += len(alts)
+    widths = [f.width / f.boundary for fs in ref.flags for f in fs if f.boundary > 0]
+    say(label, f"B={len(num)} exact={int(ok.sum())} flagged={int((~ok).sum())}",
+        f"(each in its admissible set; {n_alt} outcomes; widest band",
+        f"{max(widths) if widths else 0:.1e} relative) mean_accepted={num.mean():.3f}")
+    return ref
+
+
+def check_tree_sampled(d, al, path, out, temperature=1.0, band=TEST_BAND, label=""):
+    """Every sequence of a sampled tree acceptance against the oracle, as
+    check_chain: exact when unflagged, else one of the admissible outcomes."""
+    from oracle.accept import tree_accept_sampled, tree_sampled_admissible
+    args = (f64(d["target_logits"]), f64(d["draft_logits"]), i64(d["tokens"]),
+            i64(d["parents"]), f64(d["u_accept"]), f64(d["u_draw"]))
+    ref = tree_accept_sampled(*args, temperature=temperature, band=band)
+    al, path, out = i64(al), i64(path), i64(out)
+    ok = ~ref.near_boundary
+    mism = ok & ((al != ref.accept_len) | np.any(path != ref.path, axis=1)
+                 | np.any(out != ref.out_tokens, axis=1))
+    assert not mism.any(), np.nonzero(mism)[0][:10]
+    assert not ref.empty_ambiguous.any(), np.nonzero(ref.empty_ambiguous)[0]
+    n_alt = 0
+    for b in np.flatnonzero(~ok):
+        alts = tree_sampled_admissible(*args, b, temperature=temperature, band=band)
+        got = (int(al[b]), tuple(int(t) for t in path[b]), tuple(int(t) for t in out[b]))
+        assert got in alts, (b, got, sorted(alts), ref.flags[b])
+        n_alt += len(alts)
+    say(label, f"B={len(al)} exact={int(ok.sum())} flagged={int((~ok).sum())}",
+        f"(each in its admissible set; {n_alt} outcomes) mean_accepted={al.mean():.3f}")
+    return ref

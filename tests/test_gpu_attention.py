@@ -3,7 +3,9 @@
 Reduced sizes (several key tiles and splits, a ragged tail) are compared
 element by element; the full reference sizes, in the launch configuration the
 bench times, are compared on sampled output rows.  Tolerances: max-abs 1e-4
-for fp32 inputs, 2e-2 for bf16 K/V.
+for fp32 inputs, 2e-2 for bf16 K/V, and in both cases a largest error within
+a fraction (1e-3 fp32, 0.1 bf16) of the reference output's rms, which at long
+prefixes is itself below the max-abs contract.
 """
 import zlib
 
@@ -11,7 +13,7 @@ import numpy as np
 import pytest
 import torch
 
-from gpu_support import BF16_ATOL, F32_ATOL, device, f64, say
+from gpu_support import assert_attention_close, device, f64, say
 from oracle.attention import verify_attention
 from verify_pass_rejection_amd import inputs as I
 from verify_pass_rejection_amd import native as nat
@@ -42,12 +44,9 @@ def run_case(w, parents=None, rows=None, atol=None):
                 want.append(o[0, t, h])
                 got.append(f64(out[b, t, h]))
         got, want = np.array(got), np.array(want)
-    tol = atol if atol is not None else (F32_ATOL if w.dtype == "f32" else BF16_ATOL)
-    err = float(np.max(np.abs(got - want)))
-    say(w.name, f"B={w.B} T={w.T} Hq={w.Hq} Hkv={w.Hkv} D={w.D} ctx={w.ctx} {w.dtype}",
-        f"max_abs_err={err:.3e} tol={tol}")
-    assert np.all(np.isfinite(got))
-    assert err <= tol
+    assert_attention_close(got, want, w.dtype, atol=atol,
+                           label=f"{w.name} B={w.B} T={w.T} Hq={w.Hq} Hkv={w.Hkv} D={w.D} "
+                                 f"ctx={w.ctx} {w.dtype}")
     return out
 
 

@@ -19,7 +19,7 @@ import numpy as np
 import pytest
 import torch
 
-from gpu_support import BF16_ATOL, F32_ATOL, device, f64, say
+from gpu_support import assert_attention_close, device, f64, say
 from oracle.paged import verify_attention_paged
 from verify_pass_rejection_amd import inputs as I
 from verify_pass_rejection_amd import native as nat
@@ -99,11 +99,7 @@ def _ragged_case(w, page_size, layout, rows=None, atol=None):
                 want.append(o[0, t, h])
                 got.append(f64(out[b, t, h]))
         got, want = np.array(got), np.array(want)
-    tol = atol if atol is not None else (F32_ATOL if w.dtype == "f32" else BF16_ATOL)
-    err = float(np.max(np.abs(got - want)))
-    say(w.name, f"max_abs_err={err:.3e} tol={tol}")
-    assert np.all(np.isfinite(got))
-    assert err <= tol
+    assert_attention_close(got, want, w.dtype, label=w.name, atol=atol)
 
 
 @pytest.mark.parametrize("name,kw,page_size,layout", [

@@ -1,12 +1,15 @@
 """GPU parity of spec_accept_tree_sampled against oracle.accept.tree_accept_sampled.
 
-Accepted lengths, paths and emitted tokens must match the oracle exactly on
-every sequence whose decisions are not flagged.  The kernel takes its
-decisions in float64 from probabilities accurate to about 2 float32 ulp; the
-oracle flags a decision when its uniform lies within the band 1e-6 (relative)
-plus the error that probabilities within PROB_REL_ERR (1e-6, relative) can
-cause in the tested quantity.  Flag counts are printed.  A χ² law test runs
-the kernel itself on 2·10^5 sampled trees.
+Every sequence is checked.  The kernel takes its decisions in float64 from
+probabilities accurate to about 3 float32 roundings; the oracle carries that
+error (oracle.accept.tree_row_model) through the residual masses of the walk
+and flags a decision whose uniform lies within the propagated error of its
+boundary plus a 1e-6 relative margin.  An unflagged sequence must match the
+oracle exactly (accepted length, path, emitted tokens); a flagged one must
+match one of the oracle's admissible outcomes (the oracle rerun with each
+flagged uniform moved to either side of its boundary).  Flag counts are
+printed and stay below 15 %.  A χ² law test runs the kernel itself on 2·10^5
+sampled trees.
 """
 import numpy as np
 import pytest
@@ -14,14 +17,11 @@ import torch
 from scipy import stats
 from scipy.special import softmax as sp_softmax
 
-from gpu_support import device, f64, i64, say
-from oracle.accept import tree_accept_sampled
+from gpu_support import check_tree_sampled, device, f64, i64, say
 from verify_pass_rejection_amd import inputs as I
 from verify_pass_rejection_amd import native as nat
 
 pytestmark = pytest.mark.gpu
-
-TEST_BAND = 1e-6
 
 
 def compare(d, temperature=1.0, label=""):
@@ -29,19 +29,10 @@ def compare(d, temperature=1.0, label=""):
         d["target_logits"], d["draft_logits"], d["tokens"], d["parents"], d["u_accept"],
         d["u_draw"], temperature=temperature)
     torch.cuda.synchronize()
-    ref = tree_accept_sampled(f64(d["target_logits"]), f64(d["draft_logits"]), i64(d["tokens"]),
-                              i64(d["parents"]), f64(d["u_accept"]), f64(d["u_draw"]),
-                              temperature=temperature, band=TEST_BAND)
+    ref = check_tree_sampled(d, al, path, out, temperature=temperature, label=label)
+    assert ref.near_boundary.mean() < 0.15
     al, path, out = i64(al), i64(path), i64(out)
-    ok = ~ref.near_boundary
-    mism = ok & ((al != ref.accept_len) | np.any(path != ref.path, axis=1)
-                 | np.any(out != ref.out_tokens, axis=1))
-    say(label, f"B={len(al)} flagged={int((~ok).sum())} mismatched={int(mism.sum())}",
-        f"mean_accepted={al.mean():.3f}")
-    assert not mism.any(), np.nonzero(mism)[0][:10]
-    assert (~ok).mean() < 0.15
-    # what the oracle does not fix on flagged sequences is still well formed
-    for b in range(len(al)):
+    for b in range(len(al)):                      # every sequence is well formed
         n = al[b]
         assert path[b, 0] == 0 and np.all(path[b, n + 1:] == -1) and np.all(out[b, n + 1:] == -1)
         assert 0 <= out[b, n] < d["target_logits"].shape[2]
