@@ -97,6 +97,11 @@ const char* spec_status_string(spec_status status);
  * Limits: 1 <= T <= 64, D in {64, 128}, Hkv >= 1, Hq % Hkv == 0, ctx >= 0,
  * (ctx + T)·D < 2^31, B·Hkv <= SPEC_MAX_ROWS; q, k, v and out 16-byte aligned
  * (SPEC_ERR_UNSUPPORTED otherwise).
+ *
+ * The workspace query takes the element type too: bf16 inputs run the
+ * matrix-core kernel and fp32 inputs the vector kernel, whose key splits (and
+ * so the partial results the workspace holds) differ.  It returns 0 for
+ * arguments the call would reject and for empty problems.
  * ------------------------------------------------------------------------- */
 size_t spec_verify_attention_workspace(int B, int T, int Hq, int Hkv, int D, int ctx,
                                        spec_dtype dtype);
