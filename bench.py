@@ -12,9 +12,11 @@ verification overhead α = (T(N) − T(0)) / (N·T(0)) at N = 4 and 8 on the sam
 shape, a roofline entry for the attention kernel and the CPU oracle's rate on a
 bounded sample of the same workload.  Beside the line's own figures: the
 attention call over a paged copy of the same cache (pages of 16 positions),
-for trees the KV commit of the accepted path and the sampled (non-greedy)
-acceptance of the same tree shape, and for chains the n-gram draft proposal
-over histories of the same batch and length.
+the n-gram draft proposal over histories of the same batch and length, and
+under "other_workloads" the other reference workloads at full size with the
+cache flushed between steps (the Llama-3-8B-shaped chain with its alpha at
+N = 4 and 8, the EAGLE-2 and Medusa trees with their matrix rate, KV commit
+and sampled acceptance, and the tiny fp32 chain).
 """
 from __future__ import annotations
 
@@ -306,38 +308,86 @@ def time_ngram(w, dev, steps: int, flush=None, n_min: int = 1, n_max: int = 4):
             "note": "latency-bound: a few MB per call"}
 
 
-def cpu_baseline(w, step, budget_s: float = 30.0):
-    """The fp64 oracle on a bounded sample: sequence 0 of the same batch
-    (attention for all its heads and positions, then its acceptance)."""
+def host_info():
+    """CPU model and RAM of the host, from /proc."""
+    model, ram = "unknown", 0
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+        for line in open("/proc/meminfo"):
+            if line.startswith("MemTotal"):
+                ram = int(line.split()[1]) * 1024
+                break
+    except OSError:
+        pass
+    return model, ram
+
+
+def cpu_baseline(w, step, budget_s: float = 20.0, max_workers: int = 16):
+    """The fp64 oracle on a bounded sample of the same workload, spread over
+    the host's cores: one worker thread per core (at most max_workers, the
+    host share of one GPU), BLAS held to one thread in each, every task one
+    independent unit — a (sequence, KV head) attention unit over the whole
+    prefix, or one sequence's chain acceptance over its 2N + 1 rows.
+    Sequences are taken in order, a group of them at a time, until the budget
+    is spent; the rate is the algorithmic bytes of the sequences done per
+    second, host copies included."""
+    from concurrent.futures import ThreadPoolExecutor
+
     import numpy as np
     import torch
-    from threadpoolctl import threadpool_info
+    from threadpoolctl import threadpool_limits
 
     from oracle.accept import chain_accept
     from oracle.attention import verify_attention
 
-    f64 = lambda t: t.detach().cpu().to(torch.float64).numpy()   # noqa: E731
+    workers = max(1, min(len(os.sched_getaffinity(0)), max_workers))
+    G = w.Hq // w.Hkv
+    d = step.d
+
+    def f64(t):
+        return t.to(torch.float64).numpy()
+
+    def attention_unit(host, g):
+        q, k, v = host
+        verify_attention(f64(q[:, :, g * G:(g + 1) * G]), f64(k[:, g:g + 1]),
+                         f64(v[:, g:g + 1]), w.ctx)
+
+    def acceptance(host):
+        zp, zq, x, ua, ud = host
+        chain_accept(f64(zp), f64(zq), x.numpy(), f64(ua), f64(ud))
+
+    group = max(1, workers // w.Hkv)
     n_seq = 0
     t0 = time.perf_counter()
-    while n_seq < w.B:
-        b = n_seq
-        verify_attention(f64(step.q[b:b + 1]), f64(step.k[b:b + 1]), f64(step.v[b:b + 1]), w.ctx)
-        d = step.d
-        chain_accept(f64(d["target_logits"][b:b + 1]), f64(d["draft_logits"][b:b + 1]),
-                     d["draft_tokens"][b:b + 1].cpu().numpy(), f64(d["u_accept"][b:b + 1]),
-                     f64(d["u_draw"][b:b + 1]))
-        n_seq += 1
-        if time.perf_counter() - t0 > budget_s / 2:
-            break
+    with threadpool_limits(1), ThreadPoolExecutor(workers) as ex:
+        while n_seq < w.B and time.perf_counter() - t0 < budget_s:
+            seqs = range(n_seq, min(w.B, n_seq + group))
+            futs = []
+            for b in seqs:
+                sl = slice(b, b + 1)
+                host = (step.q[sl].cpu(), step.k[sl].cpu(), step.v[sl].cpu())
+                futs += [ex.submit(attention_unit, host, g) for g in range(w.Hkv)]
+                acc = (d["target_logits"][sl].cpu(), d["draft_logits"][sl].cpu(),
+                       d["draft_tokens"][sl].cpu(), d["u_accept"][sl].cpu(),
+                       d["u_draw"][sl].cpu())
+                futs.append(ex.submit(acceptance, acc))
+            for f in futs:
+                f.result()
+            n_seq += len(seqs)
     dt = time.perf_counter() - t0
     per_seq = (attention_bytes(w) + sampler_bytes(w)) / w.B
-    threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
-    return {"value": round(per_seq * n_seq / dt / 1e9, 4), "unit": "GB/s", "cores": threads,
+    model, ram = host_info()
+    return {"value": round(per_seq * n_seq / dt / 1e9, 4), "unit": "GB/s", "cores": workers,
             "kind": "oracle",
-            "sample": f"{n_seq} of {w.B} sequences of {w.name} (attention for all "
-                      f"{w.Hq} heads x {w.T} positions over ctx {w.ctx}, then chain "
-                      f"acceptance over {2 * w.N + 1} rows of V={w.V}); host-to-numpy copies "
-                      f"included; {dt:.1f} s"}
+            "sample": f"{n_seq} of {w.B} sequences of {w.name} (attention for all {w.Hq} heads "
+                      f"x {w.T} positions over ctx {w.ctx}, then chain acceptance over "
+                      f"{2 * w.N + 1} rows of V={w.V}); {workers} worker threads, one "
+                      f"(sequence, KV head) unit or one sequence's acceptance per task, BLAS "
+                      f"one thread each; host copies included; {dt:.1f} s",
+            "host_cpus_visible": os.cpu_count(), "cpu_model": model, "host_ram_bytes": ram}
 
 
 def source_sha256(path: str) -> str:
@@ -383,6 +433,90 @@ def copy_calibration(dev):
     torch.cuda.empty_cache()
 
 
+def measure_alpha(w, dev, step, rounds: int, flush=None):
+    """alpha at N = 4 and 8 on the workload's shape: T(N) for N = 0, 4, 8 and
+    the workload's own N, interleaved two steps at a time over many rounds
+    (the box's speed drifts by a few per cent over seconds, more than alpha
+    itself); the median step time of each N enters alpha."""
+    import torch
+    ns = sorted({0, 4, 8, w.N})
+    steps_n = {n: (step if n == w.N else Step(w.with_(T=n + 1), dev)) for n in ns}
+    for n in ns:
+        time_steps(steps_n[n], 1, 2, flush)
+    per_n = {n: [] for n in ns}
+    for _ in range(rounds):
+        for n in ns:
+            per_n[n].append(time_steps(steps_n[n], 2, 0, flush)["ms_per_step"])
+    times = {n: pct(per_n[n], 0.5) for n in ns}
+    steps_n = None
+    torch.cuda.empty_cache()
+    out = {f"alpha_N{n}": round(alpha(times[n], times[0], n), 4) for n in ns if n > 0}
+    out["verify_step_us_by_N"] = {str(n): round(times[n] * 1e3, 2) for n in ns}
+    return out
+
+
+def flush_buffer(w, dev):
+    """A 512 MB buffer to read between steps when the workload's inputs could
+    stay in L2 + the 256 MB MALL (everything below 2 GB), else None."""
+    import torch
+    if attention_bytes(w) + sampler_bytes(w) < (2 << 30):
+        return torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    return None
+
+
+def step_figures(w, step, t):
+    """Per-call figures of a timed workload: step, attention and acceptance
+    times (mean and p10/p50/p90), algorithmic GB/s and fractions of the HBM
+    peak, and the attention call's matrix rate against the bf16 MFMA peak."""
+    ab, sb = attention_bytes(w), sampler_bytes(w)
+    attn_gbps = ab / (t["attn_ms"] * 1e-3) / 1e9
+    samp_gbps = sb / (t["accept_ms"] * 1e-3) / 1e9
+    attn_tflops = attention_flops(w) / (t["attn_ms"] * 1e-3) / 1e12
+    return {
+        "verify_step_us": round(t["ms_per_step"] * 1e3, 2),
+        "attn_us": round(t["attn_ms"] * 1e3, 2),
+        "sampler_us": round(t["accept_ms"] * 1e3, 2),
+        "attn_us_p10_p50_p90": [round(x * 1e3, 2) for x in t["attn_pct_ms"]],
+        "sampler_us_p10_p50_p90": [round(x * 1e3, 2) for x in t["accept_pct_ms"]],
+        "acceptance": "greedy tree" if w.kind == "tree" else "chain rejection sampling",
+        "mean_accepted": round(float(step.num.float().mean()), 3),
+        "attn_bytes": ab, "sampler_bytes": sb,
+        "attn_GBps": round(attn_gbps, 1),
+        "sampler_GBps": round(samp_gbps, 1),
+        "attn_frac_hbm_peak": round(attn_gbps / HBM_PEAK_GBPS, 4),
+        "sampler_frac_hbm_peak": round(samp_gbps / HBM_PEAK_GBPS, 4),
+        "attn_TFLOPs": round(attn_tflops, 2),
+        "attn_frac_bf16_mfma_peak": (round(attn_tflops / BF16_MFMA_PEAK_TFLOPS, 4)
+                                     if w.dtype == "bf16" else None),
+    }
+
+
+def measure_config(name, dev, steps: int, warmup: int, with_alpha: bool):
+    """One of the other reference workloads at its full size, cache flushed
+    between steps: the step figures, alpha on chains, and for trees the KV
+    commit and the sampled (non-greedy) acceptance of the same tree shape."""
+    import torch
+    from verify_pass_rejection_amd import inputs as I
+    w = I.WORKLOADS[name]
+    flush = flush_buffer(w, dev)
+    step = Step(w, dev)
+    t = time_steps(step, steps, warmup, flush)
+    out = {"config": {"batch": w.B, "N_or_T": w.N if w.kind == "chain" else w.T, "Hq": w.Hq,
+                      "Hkv": w.Hkv, "head_dim": w.D, "ctx": w.ctx, "vocab": w.V,
+                      "kv_dtype": w.dtype},
+           "cache_flush_between_steps": flush is not None, **step_figures(w, step, t)}
+    if w.dtype == "f32":
+        out["note"] = "launch-bound correctness workload (1 MB of attention bytes)"
+    if with_alpha and w.kind == "chain":
+        out.update(measure_alpha(w, dev, step, max(40, steps), flush))
+    if w.kind == "tree":
+        out["kv_commit"] = time_commit(step, steps)
+        out["sampled_tree_acceptance"] = time_sampled_tree(w, dev, steps, flush)
+    del step, flush
+    torch.cuda.empty_cache()
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -392,6 +526,8 @@ def main():
     ap.add_argument("--no-alpha", action="store_true")
     ap.add_argument("--no-paged", action="store_true",
                     help="skip the paged-KV attention timing")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="time only the headline workload, not the other reference workloads")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (for scaling byte counters)")
     ap.add_argument("--workload", default=WORKLOAD,
@@ -411,43 +547,17 @@ def main():
     if args.copy_calibration:
         copy_calibration(dev)
     w = I.WORKLOADS[args.workload]
-    # Workloads whose inputs could sit in L2 + the 256 MB MALL get a 512 MB
-    # buffer read between steps (the large-batch chain streams 9 GB).
-    flush = None
-    if attention_bytes(w) + sampler_bytes(w) < (2 << 30):
-        flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    flush = flush_buffer(w, dev)
     step = Step(w, dev)
     t = time_steps(step, args.steps, args.warmup, flush)
-    mean_accepted = float(step.num.float().mean())
-
+    fig = step_figures(w, step, t)
     ab, sb = attention_bytes(w), sampler_bytes(w)
-    attn_gbps = ab / (t["attn_ms"] * 1e-3) / 1e9
-    samp_gbps = sb / (t["accept_ms"] * 1e-3) / 1e9
     step_gbps = (ab + sb) / (t["ms_per_step"] * 1e-3) / 1e9
+    attn_gbps = fig["attn_GBps"]
 
     alphas = {}
     if not args.no_alpha and w.kind == "chain":
-        # T(N) for N = 0, 4, 8 and the workload's own N, interleaved two steps
-        # at a time over many rounds (the box's speed drifts by a few per cent
-        # over seconds, more than alpha itself); the median step time of each
-        # N enters alpha.
-        ns = sorted({0, 4, 8, w.N})
-        steps_n = {n: (step if n == w.N else Step(w.with_(T=n + 1), dev)) for n in ns}
-        for n in ns:
-            time_steps(steps_n[n], 1, 2, flush)
-        per_n = {n: [] for n in ns}
-        for _ in range(max(40, args.steps)):
-            for n in ns:
-                tn = time_steps(steps_n[n], 2, 0, flush)
-                per_n[n].append(tn["ms_per_step"])
-        times = {n: pct(per_n[n], 0.5) for n in ns}
-        for n in ns:
-            if n != w.N:
-                del steps_n[n]
-        steps_n = None
-        torch.cuda.empty_cache()
-        alphas = {f"alpha_N{n}": round(alpha(times[n], times[0], n), 4) for n in ns if n > 0}
-        alphas["verify_step_us_by_N"] = {str(n): round(times[n] * 1e3, 2) for n in ns}
+        alphas = measure_alpha(w, dev, step, max(40, args.steps), flush)
 
     paged = None if args.no_paged else time_paged(step, args.steps, flush)
 
@@ -461,8 +571,17 @@ def main():
     cpu = None
     if not args.no_cpu_baseline and w.kind == "chain":
         cpu = cpu_baseline(w, step)
+    flushed = flush is not None
+    del step, flush
+    torch.cuda.empty_cache()
 
-    attn_tflops = attention_flops(w) / (t["attn_ms"] * 1e-3) / 1e12
+    configs = {}
+    if not args.no_configs:
+        for name in I.WORKLOADS:
+            if name != w.name:
+                configs[name] = measure_config(name, dev, args.steps, args.warmup,
+                                               with_alpha=not args.no_alpha)
+
     line = {
         "metric": METRIC,
         "value": round(step_gbps, 2),
@@ -478,23 +597,10 @@ def main():
         "data": "synthetic (seeded; stands in for the pages' unnamed chat/code workloads)",
         "config": {"workload": w.name, "batch": w.B, "N": w.N, "Hq": w.Hq, "Hkv": w.Hkv,
                    "head_dim": w.D, "ctx": w.ctx, "vocab": w.V, "kv_dtype": w.dtype},
-        "verify_step_us": round(t["ms_per_step"] * 1e3, 2),
-        "attn_us": round(t["attn_ms"] * 1e3, 2),
-        "sampler_us": round(t["accept_ms"] * 1e3, 2),
-        "attn_us_p10_p50_p90": [round(x * 1e3, 2) for x in t["attn_pct_ms"]],
-        "sampler_us_p10_p50_p90": [round(x * 1e3, 2) for x in t["accept_pct_ms"]],
-        "cache_flush_between_steps": flush is not None,
-        "acceptance": "greedy tree" if w.kind == "tree" else "chain rejection sampling",
-        "mean_accepted": round(mean_accepted, 3),
-        "attn_GBps": round(attn_gbps, 1),
-        "sampler_GBps": round(samp_gbps, 1),
-        "attn_frac_hbm_peak": round(attn_gbps / HBM_PEAK_GBPS, 4),
-        "sampler_frac_hbm_peak": round(samp_gbps / HBM_PEAK_GBPS, 4),
-        "attn_TFLOPs": round(attn_tflops, 2),
-        "attn_frac_bf16_mfma_peak": (round(attn_tflops / BF16_MFMA_PEAK_TFLOPS, 4)
-                                     if w.dtype == "bf16" else None),
+        **fig,
+        "cache_flush_between_steps": flushed,
         **alphas,
-        "roofline": {"bound": "hbm", "achieved": round(attn_gbps, 1), "peak": HBM_PEAK_GBPS,
+        "roofline": {"bound": "hbm", "achieved": attn_gbps, "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(attn_gbps / HBM_PEAK_GBPS, 4),
                      "traffic": measured_traffic() if w.name == WORKLOAD else None,
                      "kernel": ("attn_mfma_kernel (spec_verify_attention: one launch, one "
@@ -512,6 +618,8 @@ def main():
         line["sampled_tree_acceptance"] = sampled
     if ngram is not None:
         line["ngram_proposal"] = ngram
+    if configs:
+        line["other_workloads"] = configs
     print(json.dumps(line), flush=True)
 
 
