@@ -57,12 +57,19 @@ typedef enum {
     SPEC_ERR_SHAPE = 2,        /* a size is negative or inconsistent              */
     SPEC_ERR_UNSUPPORTED = 3,  /* valid but outside the supported limits          */
     SPEC_ERR_WORKSPACE = 4,    /* workspace_bytes below the queried size          */
-    SPEC_ERR_HIP = 5           /* the HIP runtime reported a launch error         */
+    SPEC_ERR_HIP = 5,          /* the HIP runtime reported a launch error         */
+    /* Not statuses: every int32 is a valid value of the type, so a C caller may
+       pass any integer to spec_status_string. */
+    SPEC_STATUS_INT32_MIN_ = -0x7fffffff - 1,
+    SPEC_STATUS_INT32_MAX_ = 0x7fffffff
 } spec_status;
 
 typedef enum {
     SPEC_F32 = 0,              /* IEEE binary32                                   */
-    SPEC_BF16 = 1              /* bfloat16 (upper half of a binary32)             */
+    SPEC_BF16 = 1,             /* bfloat16 (upper half of a binary32)             */
+    /* not types: any int32 may be passed (others give SPEC_ERR_UNSUPPORTED) */
+    SPEC_DTYPE_INT32_MIN_ = -0x7fffffff - 1,
+    SPEC_DTYPE_INT32_MAX_ = 0x7fffffff
 } spec_dtype;
 
 /* Supported limits. */
@@ -149,7 +156,10 @@ spec_status spec_verify_attention(const void* q, const void* k, const void* v,
  * ------------------------------------------------------------------------- */
 typedef enum {
     SPEC_PAGES_HND = 0,        /* a page holds each KV head's rows contiguously   */
-    SPEC_PAGES_NHD = 1         /* a page holds each position's KV heads together  */
+    SPEC_PAGES_NHD = 1,        /* a page holds each position's KV heads together  */
+    /* not layouts: any int32 may be passed (others give SPEC_ERR_UNSUPPORTED) */
+    SPEC_PAGES_INT32_MIN_ = -0x7fffffff - 1,
+    SPEC_PAGES_INT32_MAX_ = 0x7fffffff
 } spec_page_layout;
 
 #define SPEC_MAX_PAGE_SIZE (1 << 20)

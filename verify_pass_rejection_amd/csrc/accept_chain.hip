@@ -48,19 +48,10 @@ struct ChainArgs {
   float c2;              // log2(e) / temperature
 };
 
-#ifndef SV_STATS_THREADS
-#define SV_STATS_THREADS 512
-#endif
-#ifndef SV_STATS_CHUNK
-#define SV_STATS_CHUNK 16384
-#endif
-constexpr int kStatsThreads = SV_STATS_THREADS;
-constexpr int kStatsChunk = SV_STATS_CHUNK;   // logits per stats block
-#ifndef SV_DRAW_PER
-#define SV_DRAW_PER 8
-#endif
+constexpr int kStatsThreads = 512;
+constexpr int kStatsChunk = 16384;    // logits per stats block
 constexpr int kDrawThreads = 1024;
-constexpr int kDrawPer = SV_DRAW_PER; // weights per thread per draw chunk
+constexpr int kDrawPer = 8;           // weights per thread per draw chunk
 constexpr int kDrawChunk = kDrawThreads * kDrawPer;
 // Draw chunks summed per chain_chunks block: one when a chunk per block still
 // fits one wave of resident blocks (small batches are latency-bound: more
@@ -94,18 +85,7 @@ __device__ __forceinline__ float4 load_stream4(const float* p) {
   }
 }
 
-#ifndef SV_DRAW_NT
-#define SV_DRAW_NT 0
-#endif
-__device__ __forceinline__ float4 load_draw4(const float* p) {
-#if SV_DRAW_NT
-  typedef float f32x4_nt __attribute__((ext_vector_type(4)));
-  const f32x4_nt v = __builtin_nontemporal_load((const f32x4_nt*)p);
-  return make_float4(v[0], v[1], v[2], v[3]);
-#else
-  return *(const float4*)p;
-#endif
-}
+__device__ __forceinline__ float4 load_draw4(const float* p) { return *(const float4*)p; }
 
 // (m, s) pairs: s = sum 2^((z - m) c).
 __device__ __forceinline__ void merge_ms(float& m, float& s, float m2, float s2, float c) {

@@ -109,13 +109,6 @@ __device__ __forceinline__ bool tail_visible(uint64_t mask, int key, int ctx) {
   return key < ctx || ((mask >> (key - ctx)) & 1ull);
 }
 
-#ifndef SV_SETTLE_VALU
-#define SV_SETTLE_VALU 1
-#endif
-#ifndef SV_VALU_WAVES_PER_EU
-#define SV_VALU_WAVES_PER_EU 1
-#endif
-
 // Lambdas of the kernels are always inlined: an out-of-line call inside the
 // key loop would make the compiler drain every outstanding load at its return.
 #define SV_INLINE __attribute__((always_inline))
@@ -166,7 +159,7 @@ __device__ __forceinline__ float group_sum(float v) {
 
 template <int D, int RMAX, bool PAGED>
 __global__ __launch_bounds__(256)
-__attribute__((amdgpu_waves_per_eu(RMAX <= 4 ? SV_VALU_WAVES_PER_EU : 1)))
+__attribute__((amdgpu_waves_per_eu(1)))
 void attn_valu_kernel(AttnArgs a) {
   constexpr int EPL = 4;                      // fp32 elements per lane per 16-byte load
   constexpr int LPK = D / EPL;                // lanes sharing one key row
@@ -205,10 +198,8 @@ void attn_valu_kernel(AttnArgs a) {
     }
   }
   // Q stays in registers for the whole key loop: wait for it here.
-#if SV_SETTLE_VALU
 #pragma unroll
   for (int r = 0; r < RMAX; ++r) settle(qw[r]);
-#endif
 
   // This block's keys, cut into 4 contiguous per-wave ranges (a split past
   // the end of a shorter paged sequence has none).
@@ -412,9 +403,6 @@ struct MfmaLayout {
 // Ring depth: four slots (72 KB at D = 128) keep two blocks per CU resident
 // for one-row-tile kernels; five or six for the larger ones (one block per CU).  The
 // loader's outstanding loads, (AHEAD - 1) * NIT, must fit the 6-bit vmcnt.
-#ifndef SV_MFMA_LAG
-#define SV_MFMA_LAG 1
-#endif
 template <int D, int RT>
 struct MfmaRing {
   // LAG: with two compute waves per SIMD (more than four compute waves), the
@@ -423,7 +411,7 @@ struct MfmaRing {
   // tree (three row tiles) 104.8 -> 97.8 us; eagle2 tree (two row tiles)
   // 94.8 -> 91.8 us once the softmax had shed its per-tile row reduction
   // (before that, two-row-tile kernels were slower lagged).
-  static constexpr bool LAG = RT >= 2 && SV_MFMA_LAG;
+  static constexpr bool LAG = RT >= 2;
   static constexpr int P = RT == 1 ? 4 : LAG ? 6 : 5;
   static constexpr int AHEAD_MAX = 63 / MfmaLayout<D>::NIT + 1;   // (AHEAD-1)*NIT < 64
   static constexpr int AHEAD = (LAG ? P - 2 : P - 1) < AHEAD_MAX ? (LAG ? P - 2 : P - 1)
@@ -433,17 +421,10 @@ struct MfmaRing {
 
 // One direct load of 16 bytes per lane into LDS at byte offset lds (wave-
 // uniform; lane L writes lds + 16L).  M0 carries the LDS address; the nop
-// covers the M0-write to LDS-DMA hazard.  K and V are read once: SV_KV_NT
-// marks the loads non-temporal.
-#ifndef SV_KV_NT
-#define SV_KV_NT 1
-#endif
+// covers the M0-write to LDS-DMA hazard.  K and V are read once: the loads
+// are non-temporal.
 __device__ __forceinline__ void lds_dma16(const void* g, uint32_t lds) {
-#if SV_KV_NT
   asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off nt" ::"v"(g), "{m0}"(lds) : "memory");
-#else
-  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "{m0}"(lds) : "memory");
-#endif
 }
 // The same with 4 bytes per lane (lane L writes lds + 4L): page ids.
 __device__ __forceinline__ void lds_dma4(const void* g, uint32_t lds) {
@@ -940,18 +921,10 @@ static void launch_main(const AttnPlan& p, const AttnArgs& a, hipStream_t st, di
 // workspace query and the launch always agree.  The block targets aim at one
 // full wave of resident blocks on the 256 CUs: the MFMA kernel's LDS ring
 // admits two blocks per CU with one row tile per wave, one block otherwise.
-#ifndef SV_MFMA_BLOCKS_RT1
-#define SV_MFMA_BLOCKS_RT1 512
-#endif
-#ifndef SV_MFMA_BLOCKS
-#define SV_MFMA_BLOCKS 256
-#endif
-#ifndef SV_VALU_BLOCKS
-#define SV_VALU_BLOCKS 512
-#endif
-#ifndef SV_MIN_CHUNK
-#define SV_MIN_CHUNK 256
-#endif
+constexpr int kMfmaBlocksRT1 = 512;   // one row tile per wave: two blocks per CU
+constexpr int kMfmaBlocks = 256;      // larger row tiles: one block per CU
+constexpr int kValuBlocks = 512;
+constexpr int kMinChunk = 256;        // fewest keys per split
 AttnPlan plan_attention(int B, int T, int Hq, int Hkv, int D, int ctx, int bf16) {
   AttnPlan p{};
   const int G = Hq / Hkv, R = G * T, L = ctx + T, units = B * Hkv;
@@ -971,16 +944,16 @@ AttnPlan plan_attention(int B, int T, int Hq, int Hkv, int D, int ctx, int bf16)
     p.row_chunks = (waves + max_waves - 1) / max_waves;
     p.waves = (waves + p.row_chunks - 1) / p.row_chunks;
     tile = kMfmaKeys;
-    blocks_target = p.rt == 1 ? SV_MFMA_BLOCKS_RT1 : SV_MFMA_BLOCKS;
+    blocks_target = p.rt == 1 ? kMfmaBlocksRT1 : kMfmaBlocks;
   } else {
     const int rr = R < 8 ? R : 8;
     p.rmax = rr <= 1 ? 1 : rr <= 2 ? 2 : rr <= 4 ? 4 : 8;
     p.waves = 4;
     p.row_chunks = (R + p.rmax - 1) / p.rmax;
     tile = 64;
-    blocks_target = SV_VALU_BLOCKS;
+    blocks_target = kValuBlocks;
   }
-  const int min_chunk = SV_MIN_CHUNK;
+  const int min_chunk = kMinChunk;
   int S = (blocks_target + units * p.row_chunks - 1) / (units * p.row_chunks);
   if (S > kCombineMaxS) S = kCombineMaxS;
   const int s_max = (L + min_chunk - 1) / min_chunk;

@@ -101,6 +101,7 @@ const char* spec_status_string(spec_status s) {
     case SPEC_ERR_UNSUPPORTED: return "arguments are outside the supported limits";
     case SPEC_ERR_WORKSPACE: return "workspace is smaller than the queried size";
     case SPEC_ERR_HIP: return "the HIP runtime reported a launch error";
+    default: break;
   }
   return "unknown status";
 }
