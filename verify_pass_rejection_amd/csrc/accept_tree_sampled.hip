@@ -63,6 +63,11 @@ struct STreeArgs {
   float k2f;               // the same, rounded to float32
 };
 
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+// Word 3 of a raw buffer resource on gfx9-family parts: 32-bit data format,
+// no swizzle; with stride 0 a read past num_records returns 0.
+constexpr int kBufferWord3 = 0x00020000;
+
 constexpr int kSTThreads = 512;
 constexpr int kSTWaves = kSTThreads / kWave;
 constexpr int kSTChunk = 8192;                 // logits per statistics block
@@ -199,6 +204,8 @@ __global__ __launch_bounds__(kSTThreads) void stree_walk_kernel(STreeArgs a) {
   __shared__ double ni_p[64], ni_q[64];      // and 1 / Σ e
   __shared__ double ge_p[64], ge_q[64];      // e of node i's token in its parent's rows
   __shared__ float lq[CACHED ? CH * kSTThreads : 1];
+  __shared__ double red2[CACHED ? (CH / 4) * kSTWaves : 1];   // segment totals per wave
+  __shared__ double segS[CACHED ? CH / 4 : 1];                 // and per block
   __shared__ double red[kSTWaves];
   __shared__ int redi[kSTWaves];
 
@@ -252,9 +259,13 @@ __global__ __launch_bounds__(kSTThreads) void stree_walk_kernel(STreeArgs a) {
   const int my_par = lane < T ? spar[lane] : -1;
   const bool my_ok = lane >= 1 && lane < T && my_par >= 0 && my_par < lane;
 
-  // This thread's tokens (ascending, contiguous).
-  const int chs = CACHED ? CH : (V + kSTThreads - 1) / kSTThreads;
+  // Streaming: this thread's tokens j0 .. j1 - 1 (ascending, contiguous).
+  const int chs = (V + kSTThreads - 1) / kSTThreads;
   const int j0 = min(V, tid * chs), j1 = min(V, j0 + chs);
+  // Cached: element i = 4k + e of this thread is token 4·(tid + 512k) + e, so
+  // that a wave's float4 loads cover 1 KB of consecutive tokens; segment k
+  // (elements 4k .. 4k + 3 of every thread) is tokens 2048k .. 2048k + 2047.
+  auto tok = [&](int i) -> int { return 4 * (tid + kSTThreads * (i >> 2)) + (i & 3); };
 
   float rp[CACHED ? CH : 1];
   auto q_at = [&](int i) -> float& { return lq[i * kSTThreads + tid]; };
@@ -268,38 +279,57 @@ __global__ __launch_bounds__(kSTThreads) void stree_walk_kernel(STreeArgs a) {
 
   // Reads the current node's rows as e values (cached path); the draft row
   // only when `both`.
-  auto load_rows = [&](bool both) {
+  auto load_rows = [&](bool both_in) {
     if constexpr (CACHED) {
-      if constexpr (VEC) {
+      // wave-uniform: one branch around the draft row's loads and
+      // exponentials, not one per token
+      const bool both = __builtin_amdgcn_readfirstlane((int)both_in) != 0;
+      // Buffer loads: the row's base in SGPRs, the lane's offset in one VGPR
+      // and each segment's offset in an SGPR (global loads would need an
+      // address pair per segment); reads past the row return 0 and are
+      // replaced by -inf below.
+      const __amdgpu_buffer_rsrc_t rt = __builtin_amdgcn_make_buffer_rsrc(
+          (void*)zt, (short)0, V * (int)sizeof(float), kBufferWord3);
+      const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc(
+          (void*)zq, (short)0, V * (int)sizeof(float), kBufferWord3);
+      auto load4 = [&](__amdgpu_buffer_rsrc_t r, int k, float* d) __attribute__((always_inline)) {
+        const int ofs = kSTThreads * 16 * k;
+        if constexpr (VEC) {                      // V % 4 == 0: a group is wholly in or out
+          // cast the whole vector: a bit cast of one element of it reads element 0
+          const f32x4_t x = __builtin_bit_cast(
+              f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, 16 * tid, ofs, 0));
 #pragma unroll
-        for (int i = 0; i < CH; i += 4) {
-          float4 x = make_float4(-__builtin_huge_valf(), -__builtin_huge_valf(),
-                                 -__builtin_huge_valf(), -__builtin_huge_valf());
-          float4 y = x;
-          if (j0 + i < V) {                       // V % 4 == 0 on this path
-            x = *(const float4*)(zt + j0 + i);
-            if (both) y = *(const float4*)(zq + j0 + i);
-          }
-          rp[i] = x.x; rp[i + 1] = x.y; rp[i + 2] = x.z; rp[i + 3] = x.w;
-          if (both) { q_at(i) = y.x; q_at(i + 1) = y.y; q_at(i + 2) = y.z; q_at(i + 3) = y.w; }
+          for (int e = 0; e < 4; ++e) d[e] = x[e];
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            d[e] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                                 r, 16 * tid + 4 * e, ofs, 0));
         }
-      } else {
 #pragma unroll
-        for (int i = 0; i < CH; ++i) {
-          const bool in = j0 + i < V;
-          rp[i] = in ? zt[j0 + i] : -__builtin_huge_valf();
-          if (both) q_at(i) = in ? zq[j0 + i] : -__builtin_huge_valf();
-        }
-      }
+        for (int e = 0; e < 4; ++e)
+          if (tok(4 * k + e) >= V) d[e] = -__builtin_huge_valf();
+      };
+      // One row at a time, all of its loads in flight: with both rows' loads
+      // outstanding together the compiler ran out of registers and waited for
+      // each draft-row load before issuing the next (walk 38.9 -> 46.7 us on
+      // the eagle2 tree).  The draft row's e values are formed in registers
+      // and stored to LDS once.
 #pragma unroll
-      for (int i = 0; i < CH; ++i) {
-        rp[i] = e_bulk(rp[i], mp, a.k2f);
-        if (both) q_at(i) = e_bulk(q_at(i), mq, a.k2f);
+      for (int k = 0; k < CH / 4; ++k) load4(rt, k, rp + 4 * k);
+#pragma unroll
+      for (int i = 0; i < CH; ++i) rp[i] = e_bulk(rp[i], mp, a.k2f);
+      if (both) {
+        float y[CH];
+#pragma unroll
+        for (int k = 0; k < CH / 4; ++k) load4(rq, k, y + 4 * k);
+#pragma unroll
+        for (int i = 0; i < CH; ++i) q_at(i) = e_bulk(y[i], mq, a.k2f);
       }
     }
   };
-  // residual weight (p − c q)+ of token j0 + i (cached: float32 terms; q = p
-  // and c = 1 still cancel exactly) or v (streaming)
+  // residual weight (p − c q)+ of element i (cached: float32 terms; q = p
+  // and c = 1 still cancel exactly) or of token v (streaming)
   float ipf = 1.f, iqf = 1.f, cf = 0.f;
   auto res_c = [&](int i) -> float {
     return fmaxf(rp[i] * ipf - cf * (q_at(i) * iqf), 0.f);
@@ -356,62 +386,156 @@ __global__ __launch_bounds__(kSTThreads) void stree_walk_kernel(STreeArgs a) {
     n = kept;
   }
 
-  // Draw from w = (p − c q)+ (p itself when c = 0) with u_draw[b][n].
+  // Draw from w = (p − c q)+ (p itself when c = 0) with u_draw[b][n]: the
+  // first token with positive weight whose running mass exceeds u·(total).
   if constexpr (CACHED) {
     if (!loaded) load_rows(c != 0.0);            // only c != 0 needs the draft row
   }
   cf = (float)c;
-  auto weight = [&](int i) -> double {         // token j0 + i
-    if constexpr (CACHED) return (double)(c == 0.0 ? rp[i] * ipf : res_c(i));
-    else return c == 0.0 ? (double)e_bulk(zt[j0 + i], mp, a.k2f) * ip : res_s(j0 + i);
-  };
-  double cs = 0.0;
-  if constexpr (CACHED) {
+  const double u = (double)a.u_draw[(size_t)b * T + n];
+  // c = 0 (p itself) or not: one wave-uniform branch for the whole draw
+  const bool pure = __builtin_amdgcn_readfirstlane((int)(c == 0.0)) != 0;
+
+  // Cached rows: the block totals of the 2048-token segments locate the
+  // segment holding the crossing; one block scan inside it locates the
+  // thread, and that thread's four tokens the token.
+  auto draw_cached = [&](auto pure_tag) -> int {
+    constexpr bool P = decltype(pure_tag)::value;
+    constexpr int K = CACHED ? CH / 4 : 1;
+    auto w = [&](int i) -> double { return (double)(P ? rp[i] * ipf : res_c(i)); };
+    auto quad = [&](int k) -> double {          // this thread's four tokens of segment k
+      return ((w(4 * k) + w(4 * k + 1)) + w(4 * k + 2)) + w(4 * k + 3);
+    };
+    // The wave's total of every segment: K sums per lane, halved at each step
+    // (a lane keeps half of the segments and adds its partner's share of
+    // them), then a butterfly over the lanes left holding the same segment:
+    // lane L ends with segment L / (64 / K).
+    constexpr int LOGK = K == 16 ? 4 : K == 8 ? 3 : K == 4 ? 2 : K == 2 ? 1 : 0;
+    static_assert((1 << LOGK) == K && K <= 64, "segments per lane");
     launder(rp);
+    double v[K];
 #pragma unroll
-    for (int i = 0; i < CH; ++i) cs += weight(i);     // tokens past V weigh 0
-  } else {
-    for (int i = 0; i < j1 - j0; ++i) cs += weight(i);
-  }
-  // exclusive scan of the chunk sums: within the wave, then the wave bases
-  double inc = cs;
+    for (int k = 0; k < K; ++k) v[k] = quad(k);
 #pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const double y = __shfl_up(inc, o);
-    if (lane >= o) inc += y;
-  }
-  double ex = __shfl_up(inc, 1);
-  if (lane == 0) ex = 0.0;
-  __syncthreads();
-  if (lane == 63) red[tid >> 6] = inc;
-  __syncthreads();
-  double base = 0.0;
-  for (int w = 0; w < (tid >> 6); ++w) base += red[w];
-  double total = 0.0;
+    for (int st = 0; st < LOGK; ++st) {
+      const int o = 32 >> st, c = K >> st;     // c segments per lane before this step
+      const bool up = (lane & o) != 0;
 #pragma unroll
-  for (int w = 0; w < kSTWaves; ++w) total += red[w];
-  ex += base;
-  const double thr = (double)a.u_draw[(size_t)b * T + n] * total;
-  // the weights are recomputed below rather than kept from the sum above
-  if constexpr (CACHED) launder(rp);
-  // this chunk's first token with positive weight whose running mass passes thr
-  int cand = V;
-  double run = ex;
-  if constexpr (CACHED) {
-#pragma unroll
-    for (int i = 0; i < CH; ++i) {
-      const double wi = weight(i);
-      run += wi;
-      if (cand == V && wi > 0.0 && run > thr) cand = j0 + i;
+      for (int j = 0; j < c / 2; ++j) {
+        const double keep = up ? v[j + c / 2] : v[j];
+        const double send = up ? v[j] : v[j + c / 2];
+        v[j] = keep + __shfl_xor(send, o);
+      }
     }
-  } else {
-    for (int i = 0; i < j1 - j0; ++i) {
-      const double wi = weight(i);
-      run += wi;
-      if (wi > 0.0 && run > thr) { cand = j0 + i; break; }
+#pragma unroll
+    for (int o = 32 >> LOGK; o > 0; o >>= 1) v[0] += __shfl_xor(v[0], o);
+    if ((lane & (64 / K - 1)) == 0) red2[(tid >> 6) * K + lane / (64 / K)] = v[0];
+    __syncthreads();
+    if (tid < K) {                               // segment totals: the waves in order
+      double t = 0.0;
+#pragma unroll
+      for (int w8 = 0; w8 < kSTWaves; ++w8) t += red2[w8 * K + tid];
+      segS[tid] = t;
     }
-  }
-  int y = block_min(cand, redi);
+    __syncthreads();
+    double total = 0.0;
+#pragma unroll
+    for (int k = 0; k < K; ++k) total += segS[k];
+    const double thr = u * total;
+    int ks = -1;
+    double pre = 0.0, pks = 0.0;
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+      const double t = segS[k];
+      if (ks < 0 && pre + t > thr) { ks = k; pks = pre; }
+      pre += t;
+    }
+    ks = __builtin_amdgcn_readfirstlane(ks);
+    if (ks < 0) return V;                        // a zero total: nothing to draw
+    launder(rp);
+    double mine = 0.0;
+#pragma unroll
+    for (int k = 0; k < K; ++k)
+      if (k == ks) mine = quad(k);
+    // exclusive scan of the threads' sums in segment ks: the wave, then the waves
+    double inc = mine;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const double up = __shfl_up(inc, o);
+      if (lane >= o) inc += up;
+    }
+    double ex = __shfl_up(inc, 1);
+    if (lane == 0) ex = 0.0;
+    if (lane == 63) red[tid >> 6] = inc;         // red's last readers are behind the barriers above
+    __syncthreads();
+    for (int w8 = 0; w8 < (tid >> 6); ++w8) ex += red[w8];
+    launder(rp);
+    double run = pks + ex;
+    int cand = V, last = -1;
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+      if (k != ks) continue;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const double wi = w(4 * k + e);
+        run += wi;
+        if (cand == V && wi > 0.0 && run > thr) cand = tok(4 * k + e);
+        if (wi > 0.0) last = tok(4 * k + e);
+      }
+    }
+    int y = block_min(cand, redi);
+    // Rounding can leave the scan's end of segment ks at or below thr although
+    // the segment totals put the crossing inside it: then it is the segment's
+    // last token with positive weight.
+    if (y >= V) {
+      const int lastpos = -block_min(-last, redi);
+      y = lastpos >= 0 ? lastpos : V;
+    }
+    return y;
+  };
+
+  // Streaming: each thread sums its contiguous chunk, a block scan gives every
+  // chunk its starting mass, each thread looks for the crossing in its own
+  // chunk and a block minimum picks the token.
+  auto draw_stream = [&](auto pure_tag) -> int {
+    constexpr bool P = decltype(pure_tag)::value;
+    auto w = [&](int v) -> double {
+      return P ? (double)e_bulk(zt[v], mp, a.k2f) * ip : res_s(v);
+    };
+    double cs = 0.0;
+    for (int v = j0; v < j1; ++v) cs += w(v);
+    double inc = cs;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const double y = __shfl_up(inc, o);
+      if (lane >= o) inc += y;
+    }
+    double ex = __shfl_up(inc, 1);
+    if (lane == 0) ex = 0.0;
+    __syncthreads();
+    if (lane == 63) red[tid >> 6] = inc;
+    __syncthreads();
+    double base = 0.0;
+    for (int v = 0; v < (tid >> 6); ++v) base += red[v];
+    double total = 0.0;
+#pragma unroll
+    for (int v = 0; v < kSTWaves; ++v) total += red[v];
+    ex += base;
+    const double thr = u * total;
+    // this chunk's first token with positive weight whose running mass passes thr
+    int cand = V;
+    double run = ex;
+    for (int v = j0; v < j1; ++v) {
+      const double wi = w(v);
+      run += wi;
+      if (wi > 0.0 && run > thr) { cand = v; break; }
+    }
+    return block_min(cand, redi);
+  };
+
+  int y;
+  if constexpr (CACHED) y = pure ? draw_cached(std::true_type{}) : draw_cached(std::false_type{});
+  else y = pure ? draw_stream(std::true_type{}) : draw_stream(std::false_type{});
   if (y >= V) y = V - 1;                      // nothing to draw (a zero total)
 
   __syncthreads();
