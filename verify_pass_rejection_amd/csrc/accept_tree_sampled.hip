@@ -24,8 +24,13 @@
 //                c_{j+1} q(v))+ (one pass per rejection).  For V <= 32768 the
 //                rows, once read, stay on chip while the node is visited: the
 //                target row in registers (up to 64 tokens per thread), the
-//                draft row in LDS.  The draw: each thread sums a contiguous
-//                chunk of the weights, a block scan gives every chunk its
+//                draft row in LDS, thread t holding the float4 groups t,
+//                t + 512, ... (coalesced loads).  The draw then takes the
+//                block totals of the 2048-token segments to find the segment
+//                holding the crossing, one block scan inside it to find the
+//                thread, and that thread's four tokens to find the token.
+//                For larger V the rows are streamed: each thread sums a
+//                contiguous chunk, a block scan gives every chunk its
 //                starting mass, each thread looks for the crossing in its own
 //                chunk and a block minimum picks the token.
 // Every reduction runs in a fixed order and leaves the same value in every
