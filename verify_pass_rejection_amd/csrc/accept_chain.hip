@@ -214,8 +214,7 @@ __device__ __forceinline__ void draw_weights(const DrawRow& r, int V, int chunk,
 // sequential scan of the wave totals.  prefix[e] is the running sum up to and
 // including weight e of this thread; the chunk total is prefix[kDrawPer-1] of
 // the last thread, so re-running the same scan reproduces it bit for bit.
-__device__ __forceinline__ void chunk_scan(const float* w, float* prefix, float* wave_tot,
-                                           float* wave_off) {
+__device__ __forceinline__ void chunk_scan(const float* w, float* prefix, float* wave_tot) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   float local[kDrawPer];
   local[0] = w[0];
@@ -229,14 +228,15 @@ __device__ __forceinline__ void chunk_scan(const float* w, float* prefix, float*
   }
   float excl = __shfl_up(incl, 1);
   if (lane == 0) excl = 0.f;
+  __syncthreads();                               // wave_tot is free again
   if (lane == kWave - 1) wave_tot[wave] = incl;
   __syncthreads();
-  if (threadIdx.x == 0) {
-    float acc = 0.f;
-    for (int i = 0; i < kDrawThreads / kWave; ++i) { wave_off[i] = acc; acc += wave_tot[i]; }
-  }
-  __syncthreads();
-  const float off = wave_off[wave] + excl;
+  // the wave's offset: the totals of the waves before it, added in wave order
+  // (every read issued at once; adding 0 to the others changes no bit)
+  float wo = 0.f;
+#pragma unroll
+  for (int i = 0; i < kDrawThreads / kWave; ++i) wo += i < wave ? wave_tot[i] : 0.f;
+  const float off = wo + excl;
 #pragma unroll
   for (int e = 0; e < kDrawPer; ++e) prefix[e] = off + local[e];
 }
@@ -248,7 +248,7 @@ __device__ __forceinline__ void chunk_scan(const float* w, float* prefix, float*
 // and returns k, the first rejection (N if none), to every thread.
 template <int NT>
 __device__ __forceinline__ int chain_decision(const ChainArgs& a, int b, float* row_m,
-                                              float* row_l, int* keep, int* s_k) {
+                                              float* row_l, int* s_k) {
   const int tid = threadIdx.x, N = a.N, rows = 2 * N + 1;
   const int lane = tid & 63, wave = tid >> 6;
   // The drafted tokens' logits are gathered first so that their latency
@@ -274,22 +274,20 @@ __device__ __forceinline__ int chain_decision(const ChainArgs& a, int b, float* 
     if (lane == 0) { row_m[r] = M; row_l[r] = log2f(S); }
   }
   __syncthreads();
-  if (tid < N) {
-    bool ok = false;
-    if (x >= 0 && x < a.V) {
-      const float lp = (zp - row_m[tid]) * a.c2 - row_l[tid];
-      const float lq = (zq - row_m[N + 1 + tid]) * a.c2 - row_l[N + 1 + tid];
-      const float r = exp2f(lp - lq);   // q = 0: +inf when p > 0; NaN (reject) when both 0
-      ok = a.u_acc[(size_t)b * N + tid] < r;
+  // The N <= 63 ratio tests sit in wave 0: k is its first failing lane.
+  if (wave == 0) {
+    bool ok = true;
+    if (tid < N) {
+      ok = false;
+      if (x >= 0 && x < a.V) {
+        const float lp = (zp - row_m[tid]) * a.c2 - row_l[tid];
+        const float lq = (zq - row_m[N + 1 + tid]) * a.c2 - row_l[N + 1 + tid];
+        const float r = exp2f(lp - lq);   // q = 0: +inf when p > 0; NaN (reject) when both 0
+        ok = a.u_acc[(size_t)b * N + tid] < r;
+      }
     }
-    keep[tid] = ok;
-  }
-  __syncthreads();
-  if (tid == 0) {
-    int k = N;
-    for (int i = 0; i < N; ++i)
-      if (!keep[i]) { k = i; break; }
-    *s_k = k;
+    const uint64_t rej = __ballot(!ok);
+    if (tid == 0) *s_k = rej ? __builtin_ctzll(rej) : N;
   }
   __syncthreads();
   return *s_k;
@@ -321,7 +319,7 @@ __device__ __forceinline__ void draw_rows(const ChainArgs& a, int b, int& k, Dra
 // first, then one scan per chunk (chunks past the row are not written).
 template <int VEC, int CPB, bool RESID>
 __device__ __forceinline__ void chunk_sums(const ChainArgs& a, const DrawRow& r, int b, int c0,
-                                           float* wave_tot, float* wave_off) {
+                                           float* wave_tot) {
   float xp[CPB][kDrawPer], xq[CPB][kDrawPer];
 #pragma unroll
   for (int cc = 0; cc < CPB; ++cc) draw_load<VEC, RESID>(r, a.V, c0 + cc, xp[cc], xq[cc]);
@@ -331,7 +329,7 @@ __device__ __forceinline__ void chunk_sums(const ChainArgs& a, const DrawRow& r,
     if (ch >= a.dchunks) break;
     float w[kDrawPer], pre[kDrawPer];
     draw_weights_from<RESID>(r, a.V, ch, xp[cc], xq[cc], w);
-    chunk_scan(w, pre, wave_tot, wave_off);
+    chunk_scan(w, pre, wave_tot);
     if (threadIdx.x == kDrawThreads - 1) a.csum[(size_t)b * 2 * a.dchunks + ch] = pre[kDrawPer - 1];
   }
 }
@@ -342,11 +340,11 @@ __device__ __forceinline__ void chunk_sums(const ChainArgs& a, const DrawRow& r,
 // chain_select.
 template <int VEC, int CPB>
 __global__ __launch_bounds__(kDrawThreads) void chain_chunks_kernel(ChainArgs a) {
-  __shared__ float wave_tot[kDrawThreads / kWave], wave_off[kDrawThreads / kWave];
+  __shared__ float wave_tot[kDrawThreads / kWave];
   __shared__ float row_m[128], row_l[128];
-  __shared__ int keep[64], s_k;
+  __shared__ int s_k;
   const int c = blockIdx.x, b = blockIdx.y, N = a.N;
-  const int k = chain_decision<kDrawThreads>(a, b, row_m, row_l, keep, &s_k);
+  const int k = chain_decision<kDrawThreads>(a, b, row_m, row_l, &s_k);
   DrawRow dr;
   dr.zp = a.target + ((size_t)b * (N + 1) + k) * a.V;
   dr.mp = row_m[k];
@@ -363,16 +361,16 @@ __global__ __launch_bounds__(kDrawThreads) void chain_chunks_kernel(ChainArgs a)
     a.decision[b] = make_float4(__int_as_float(k), row_m[k], row_l[k], 0.f);
     a.decision_q[b] = make_float4(dr.mq, dr.lq, 0.f, 0.f);
   }
-  if (k < N) chunk_sums<VEC, CPB, true>(a, dr, b, c * CPB, wave_tot, wave_off);
-  else chunk_sums<VEC, CPB, false>(a, dr, b, c * CPB, wave_tot, wave_off);
+  if (k < N) chunk_sums<VEC, CPB, true>(a, dr, b, c * CPB, wave_tot);
+  else chunk_sums<VEC, CPB, false>(a, dr, b, c * CPB, wave_tot);
 }
 
 template <int VEC>
 __global__ __launch_bounds__(kDrawThreads) void chain_select_kernel(ChainArgs a) {
-  __shared__ float wave_tot[kDrawThreads / kWave], wave_off[kDrawThreads / kWave];
+  __shared__ float wave_tot[kDrawThreads / kWave];
   __shared__ int wave_hit[kDrawThreads / kWave];
-  __shared__ int s_chunk, s_mode, s_y;
-  __shared__ float s_carry, s_target;
+  __shared__ int s_chunk;
+  __shared__ float s_carry, s_target, s_total;
   const int b = blockIdx.x, tid = threadIdx.x, N = a.N, nch = a.dchunks;
   const int lane = tid & 63, wave = tid >> 6;
   // The sequence's draw uniforms, its decision records and the chunk sums
@@ -383,70 +381,94 @@ __global__ __launch_bounds__(kDrawThreads) void chain_select_kernel(ChainArgs a)
   DrawRow dp, dr;
   draw_rows(a, b, k, dp, dr);
   float* cs = a.csum + (size_t)b * 2 * nch;
-  __shared__ float total_s;
   __shared__ float cs_l[kDrawThreads];
   const bool in_lds = nch <= kDrawThreads;
   if (in_lds && tid < nch) cs_l[tid] = cs[tid];           // one parallel load
   __syncthreads();
   const float u = u_l[k];
 
-  if (tid == 0) {
-    float total = 0.f;
-    for (int i = 0; i < nch; ++i) total += in_lds ? cs_l[i] : cs[i];
-    total_s = total;
-  }
+  // The chunk holding the crossing of u·total, over the chunk sums row[0..nch),
+  // found by wave 0.  The additions run in chunk order, as one thread would
+  // take them: with nch <= 64 lane i holds chunk i's sum, the running total
+  // passes from lane to lane through readlane (register to register), and
+  // the first lane whose prefix plus own sum passes the target is the chunk.
+  auto locate = [&](const float* row) {
+    if (nch <= kWave) {
+      const float ri = lane < nch ? row[min(lane, nch - 1)] : 0.f;   // clamped: in bounds
+      float acc = 0.f, run = 0.f;                 // acc: the prefix before this lane's chunk
+      for (int j = 0; j < nch; ++j) {             // nch is wave-uniform
+        if (lane == j) acc = run;
+        run += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(ri), j));
+      }
+      const float total = run;
+      const float target = u * total;
+      const uint64_t cross = __ballot(lane < nch && acc + ri > target);
+      const uint64_t mass = __ballot(lane < nch && ri > 0.f);
+      // rounding left no crossing: the last chunk with mass
+      const int cstar = cross ? __builtin_ctzll(cross) : mass ? 63 - __builtin_clzll(mass) : -1;
+      // without a crossing the prefix is the whole total, as in the serial scan
+      const float carry = cross ? __shfl(acc, cstar) : total;
+      if (lane == 0) {
+        s_total = total;
+        s_chunk = cstar;
+        s_carry = carry;
+        s_target = target;
+      }
+    } else if (lane == 0) {
+      float total = 0.f;
+      for (int i = 0; i < nch; ++i) total += row[i];
+      const float target = u * total;
+      float acc = 0.f;
+      int cstar = -1;
+      for (int i = 0; i < nch; ++i) {
+        if (acc + row[i] > target) { cstar = i; break; }
+        acc += row[i];
+      }
+      if (cstar < 0)                  // rounding left no crossing: last chunk with mass
+        for (int i = nch - 1; i >= 0; --i)
+          if (row[i] > 0.f) { cstar = i; break; }
+      s_total = total;
+      s_chunk = cstar;
+      s_carry = acc;
+      s_target = target;
+    }
+  };
+  if (wave == 0) locate(in_lds ? cs_l : cs);
   __syncthreads();
   int use = 0;
-  if (k < N && total_s == 0.f) {
+  if (k < N && s_total == 0.f) {
     // Empty residual at a rejection (possible only through rounding): the
     // chunk sums of p_k, computed here with the same scan.
     use = 1;
     for (int c = 0; c < nch; ++c) {
       float w[kDrawPer], pre[kDrawPer];
       draw_weights<VEC>(dp, a.V, c, w);
-      chunk_scan(w, pre, wave_tot, wave_off);
+      chunk_scan(w, pre, wave_tot);
       if (tid == kDrawThreads - 1) cs[nch + c] = pre[kDrawPer - 1];
       __syncthreads();
     }
     __threadfence_block();
     __syncthreads();
+    if (wave == 0) locate(cs + nch);
+    __syncthreads();
   }
-  if (tid == 0) {
-    const float* row = (use == 0 && in_lds) ? cs_l : cs + (size_t)use * nch;
-    float total = 0.f;
-    for (int i = 0; i < nch; ++i) total += row[i];
-    const float target = u * total;
-    float acc = 0.f;
-    int cstar = -1;
-    for (int i = 0; i < nch; ++i) {
-      if (acc + row[i] > target) { cstar = i; break; }
-      acc += row[i];
-    }
-    if (cstar < 0)                  // rounding left no crossing: last chunk with mass
-      for (int i = nch - 1; i >= 0; --i)
-        if (row[i] > 0.f) { cstar = i; break; }
-    s_mode = use;
-    s_chunk = cstar;
-    s_carry = acc;
-    s_target = target;
-    s_y = -1;
-  }
-  __syncthreads();
 
   // The crossing inside chunk s_chunk: the first weight whose running sum
   // exceeds u * total (or the last positive weight if rounding left none).
   const int cstar = s_chunk;
+  int y = -1;
   if (cstar >= 0) {
-    const float* row = (s_mode == 0 && in_lds) ? cs_l : cs + (size_t)s_mode * nch;
-    const bool last_mass = !(s_carry + row[cstar] > s_target);
+    const float* row = (use == 0 && in_lds) ? cs_l : cs + (size_t)use * nch;
+    const float carry = s_carry, target = s_target;
+    const bool last_mass = !(carry + row[cstar] > target);
     float w[kDrawPer], pre[kDrawPer];
-    draw_weights<VEC>(s_mode ? dp : dr, a.V, cstar, w);
-    chunk_scan(w, pre, wave_tot, wave_off);
+    draw_weights<VEC>(use ? dp : dr, a.V, cstar, w);
+    chunk_scan(w, pre, wave_tot);
     int pick = -1;
     if (!last_mass) {
 #pragma unroll
       for (int e = kDrawPer - 1; e >= 0; --e)
-        if (s_carry + pre[e] > s_target) pick = e;
+        if (carry + pre[e] > target) pick = e;
     } else {
 #pragma unroll
       for (int e = 0; e < kDrawPer; ++e)
@@ -459,25 +481,18 @@ __global__ __launch_bounds__(kDrawThreads) void chain_select_kernel(ChainArgs a)
     const int wtok = __shfl(tok, src);
     if (lane == 0) wave_hit[wave] = ballot ? wtok : -1;
     __syncthreads();
-    if (tid == 0) {
-      int y = -1;
-      if (!last_mass) {
-        for (int i = 0; i < kDrawThreads / kWave; ++i)
-          if (wave_hit[i] >= 0) { y = wave_hit[i]; break; }
-      } else {
-        for (int i = kDrawThreads / kWave - 1; i >= 0; --i)
-          if (wave_hit[i] >= 0) { y = wave_hit[i]; break; }
-      }
-      s_y = y;
-    }
-    __syncthreads();
+    // every wave: the first (or, for the last positive weight, the last) wave
+    // with a hit, from one ballot over the wave results
+    const int h = lane < kDrawThreads / kWave ? wave_hit[lane] : -1;
+    const uint64_t hits = __ballot(h >= 0);
+    if (hits) y = __shfl(h, last_mass ? 63 - __builtin_clzll(hits) : __builtin_ctzll(hits));
   }
 
   // Emit x_0..x_{k-1}, y, then -1.
   if (tid <= N) {
     int v = -1;
     if (tid < k) v = a.tokens[(size_t)b * N + tid];
-    else if (tid == k) v = s_y;
+    else if (tid == k) v = y;
     a.out[(size_t)b * (N + 1) + tid] = v;
   }
   if (tid == 0) a.num_acc[b] = k;
