@@ -316,21 +316,51 @@ __device__ __forceinline__ void draw_rows(const ChainArgs& a, int b, int& k, Dra
 }
 
 // Chunk sums of draw chunks [c0, c0 + CPB) of the drawn row: every load
-// first, then one scan per chunk (chunks past the row are not written).
+// first, then the scans of all the chunks with one barrier between their wave
+// scans and their totals (chunks past the row are not written).  A chunk's
+// total is what chunk_scan gives the last thread, with the same additions in
+// the same order, so chain_select's re-scan reproduces it bit for bit.
+// wave_tot holds CPB × (waves per block) floats.
 template <int VEC, int CPB, bool RESID>
 __device__ __forceinline__ void chunk_sums(const ChainArgs& a, const DrawRow& r, int b, int c0,
                                            float* wave_tot) {
+  constexpr int NW = kDrawThreads / kWave;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   float xp[CPB][kDrawPer], xq[CPB][kDrawPer];
 #pragma unroll
   for (int cc = 0; cc < CPB; ++cc) draw_load<VEC, RESID>(r, a.V, c0 + cc, xp[cc], xq[cc]);
+  float last[CPB], excl[CPB];
 #pragma unroll
   for (int cc = 0; cc < CPB; ++cc) {
-    const int ch = c0 + cc;
-    if (ch >= a.dchunks) break;
-    float w[kDrawPer], pre[kDrawPer];
-    draw_weights_from<RESID>(r, a.V, ch, xp[cc], xq[cc], w);
-    chunk_scan(w, pre, wave_tot);
-    if (threadIdx.x == kDrawThreads - 1) a.csum[(size_t)b * 2 * a.dchunks + ch] = pre[kDrawPer - 1];
+    last[cc] = excl[cc] = 0.f;
+    if (c0 + cc >= a.dchunks) continue;          // block-uniform
+    float w[kDrawPer];
+    draw_weights_from<RESID>(r, a.V, c0 + cc, xp[cc], xq[cc], w);
+    float l = w[0];
+#pragma unroll
+    for (int e = 1; e < kDrawPer; ++e) l = l + w[e];
+    float incl = l;
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) {
+      const float y = __shfl_up(incl, off);
+      if (lane >= off) incl += y;
+    }
+    float ex = __shfl_up(incl, 1);
+    if (lane == 0) ex = 0.f;
+    last[cc] = l;
+    excl[cc] = ex;
+    if (lane == kWave - 1) wave_tot[cc * NW + wave] = incl;
+  }
+  __syncthreads();
+  if (threadIdx.x == kDrawThreads - 1) {
+#pragma unroll
+    for (int cc = 0; cc < CPB; ++cc) {
+      if (c0 + cc >= a.dchunks) continue;
+      float wo = 0.f;
+#pragma unroll
+      for (int i = 0; i < NW - 1; ++i) wo += wave_tot[cc * NW + i];
+      a.csum[(size_t)b * 2 * a.dchunks + c0 + cc] = (wo + excl[cc]) + last[cc];
+    }
   }
 }
 
@@ -340,7 +370,7 @@ __device__ __forceinline__ void chunk_sums(const ChainArgs& a, const DrawRow& r,
 // chain_select.
 template <int VEC, int CPB>
 __global__ __launch_bounds__(kDrawThreads) void chain_chunks_kernel(ChainArgs a) {
-  __shared__ float wave_tot[kDrawThreads / kWave];
+  __shared__ float wave_tot[CPB * (kDrawThreads / kWave)];
   __shared__ float row_m[128], row_l[128];
   __shared__ int s_k;
   const int c = blockIdx.x, b = blockIdx.y, N = a.N;
