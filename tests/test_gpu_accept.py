@@ -44,6 +44,10 @@ def compare_chain(d, temperature=1.0, label=""):
     ("large_batch_chain", dict(B=32, T=64, V=777)), # N = 63
     ("large_batch_chain", dict(B=16, T=5, V=1)),    # one token: every draft kept
     ("large_batch_chain", dict(B=16, T=9, V=2)),
+    # 64 draw chunks of 8192 (the chunk search runs across one wave's lanes)
+    # and 65 (it runs in one thread)
+    ("large_batch_chain", dict(B=2, T=3, V=64 * 8192)),
+    ("large_batch_chain", dict(B=2, T=3, V=64 * 8192 + 1)),
 ])
 def test_chain_matches_oracle(name, kw):
     dev = device()

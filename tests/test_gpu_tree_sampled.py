@@ -44,6 +44,14 @@ def compare(d, temperature=1.0, label=""):
     ("medusa70b_tree", dict(B=6, V=3001)),          # V not a multiple of 4
     ("eagle2_tree", dict(B=64, V=777)),              # many sequences, chunks of one token
     ("eagle2_tree", dict(B=3, V=40000)),             # V > 32768: rows streamed per pass
+    # layout edges of the walk's cached rows (16, 32, 64 tokens per thread, in
+    # segments of 2048) and of its streamed rows just past them
+    ("eagle2_tree", dict(B=2, V=8192)),
+    ("eagle2_tree", dict(B=2, V=8193)),
+    ("eagle2_tree", dict(B=2, V=16385)),
+    ("eagle2_tree", dict(B=2, V=32767)),
+    ("eagle2_tree", dict(B=2, V=32768)),
+    ("eagle2_tree", dict(B=2, V=32769)),
     ("eagle2_tree", dict()),                         # full reference size
     ("medusa70b_tree", dict()),                      # full reference size
 ])
