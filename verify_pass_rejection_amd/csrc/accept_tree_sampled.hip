@@ -195,10 +195,11 @@ __global__ __launch_bounds__(kSTThreads) void stree_stats_kernel(STreeArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// stree_walk.  CH > 0: V <= 512·CH, a visited node's rows are read once
-// (every load in flight, float4 loads when VEC) into registers (target) and
-// LDS (draft, token j0 + i of this thread at lq[i·512 + tid]: conflict-free).
-// CH = 0: any V, every pass streams the rows from memory.
+// stree_walk.  CH > 0: V <= 512·CH, a visited node's rows are read once,
+// one row at a time with every load in flight (buffer loads; 16 bytes each
+// when VEC), into registers (target) and LDS (draft: element i of this
+// thread at lq[i·512 + tid], conflict-free); element i = 4k + e is token
+// 4·(tid + 512k) + e.  CH = 0: any V, every pass streams the rows from memory.
 // ---------------------------------------------------------------------------
 template <int CH, bool VEC>
 __global__ __launch_bounds__(kSTThreads) void stree_walk_kernel(STreeArgs a) {
