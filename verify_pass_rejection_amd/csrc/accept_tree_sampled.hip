@@ -147,51 +147,72 @@ __device__ __forceinline__ void launder(float (&r)[N]) {
 }
 
 // ---------------------------------------------------------------------------
-// stree_stats: block (chunk, row, kind); kind 0 = target rows, 1 = draft rows
-// (skipped for nodes without children: their draft rows are never used).
+// stree_stats: block (chunk, row): that chunk of the node's target row and,
+// when the node has children, of its draft row (no other draft row is ever
+// used).  Whether it has children is read (one parent per thread, a block OR)
+// while the target chunk's loads are in flight, and the draft chunk's loads
+// are in flight while the target chunk is summed.  16-byte loads when VEC, with
+// indices clamped into the row, so every load is issued before the first use.
 // Ordinary (cached) loads: the walk reads the rows of the visited nodes again
 // right after this pass, and finds them in the last-level cache.
 // ---------------------------------------------------------------------------
+template <bool VEC>
 __global__ __launch_bounds__(kSTThreads) void stree_stats_kernel(STreeArgs a) {
   __shared__ double red[kSTWaves];
   __shared__ float redf[kSTWaves];
-  const int ch = blockIdx.x, row = blockIdx.y, kind = blockIdx.z;
+  const int ch = blockIdx.x, row = blockIdx.y;
   const int b = row / a.T, node = row % a.T;
-  if (kind == 1) {
-    // does the node have a child? one parent per thread, then a block OR
-    const int i = threadIdx.x;
-    const bool mine = i > node && i < a.T && a.parents[(size_t)b * a.T + i] == node;
-    if (!__syncthreads_or(mine)) return;       // uniform: the whole block leaves
-  }
-  const float* z = (kind == 0 ? a.target : a.draft) + (size_t)row * a.V;
   const int begin = ch * kSTChunk, end = min(a.V, begin + kSTChunk);
   constexpr int PER = kSTChunk / kSTThreads;
-  float x[PER];
+  auto load = [&](const float* z, float (&x)[PER]) __attribute__((always_inline)) {
+    if constexpr (VEC) {                         // V % 4 == 0: a group is wholly in or out
 #pragma unroll
-  for (int i = 0; i < PER; ++i) {
-    const int v = begin + i * kSTThreads + threadIdx.x;
-    x[i] = v < end ? z[v] : -__builtin_huge_valf();
-  }
-  float mx = x[0];
+      for (int k = 0; k < PER / 4; ++k) {
+        const int v = begin + (k * kSTThreads + threadIdx.x) * 4;
+        const f32x4_t y = *(const f32x4_t*)(z + min(v, a.V - 4));
 #pragma unroll
-  for (int i = 1; i < PER; ++i) mx = fmaxf(mx, x[i]);
-  mx = block_max(mx, redf);
-  double s = 0.0;
-  // groups of four terms in float32 (at most 3 roundings), groups in float64;
-  // a chunk of -inf logits (a masked vocabulary range) has no mass: its
-  // maximum stays -inf and its sum 0, which the walk's merge weighs 0
-  if (mx != -__builtin_huge_valf()) {
+        for (int e = 0; e < 4; ++e) x[4 * k + e] = v < end ? y[e] : -__builtin_huge_valf();
+      }
+    } else {
 #pragma unroll
-    for (int i = 0; i < PER; i += 4)
-      s += (double)((e_bulk(x[i], mx, a.k2f) + e_bulk(x[i + 1], mx, a.k2f)) +
-                    (e_bulk(x[i + 2], mx, a.k2f) + e_bulk(x[i + 3], mx, a.k2f)));
-  }
-  s = block_sum(s, red);
-  if (threadIdx.x == 0) {
-    const size_t o = ((size_t)kind * a.B * a.T + row) * a.nchunks + ch;
-    a.part_m[o] = mx;
-    a.part_s[o] = s;
-  }
+      for (int i = 0; i < PER; ++i) {
+        const int v = begin + i * kSTThreads + threadIdx.x;
+        const float y = z[min(v, a.V - 1)];
+        x[i] = v < end ? y : -__builtin_huge_valf();
+      }
+    }
+  };
+  // the chunk's maximum and Σ e: groups of four terms in float32 (at most 3
+  // roundings), groups in float64; a chunk of -inf logits (a masked
+  // vocabulary range) has no mass: its maximum stays -inf and its sum 0,
+  // which the walk's merge weighs 0
+  auto stats = [&](const float (&x)[PER], int kind) __attribute__((always_inline)) {
+    float mx = x[0];
+#pragma unroll
+    for (int i = 1; i < PER; ++i) mx = fmaxf(mx, x[i]);
+    mx = block_max(mx, redf);
+    double s = 0.0;
+    if (mx != -__builtin_huge_valf()) {
+#pragma unroll
+      for (int i = 0; i < PER; i += 4)
+        s += (double)((e_bulk(x[i], mx, a.k2f) + e_bulk(x[i + 1], mx, a.k2f)) +
+                      (e_bulk(x[i + 2], mx, a.k2f) + e_bulk(x[i + 3], mx, a.k2f)));
+    }
+    s = block_sum(s, red);
+    if (threadIdx.x == 0) {
+      const size_t o = ((size_t)kind * a.B * a.T + row) * a.nchunks + ch;
+      a.part_m[o] = mx;
+      a.part_s[o] = s;
+    }
+  };
+  float x[PER], y[PER];
+  load(a.target + (size_t)row * a.V, x);
+  const int i = threadIdx.x;
+  const bool mine = i > node && i < a.T && a.parents[(size_t)b * a.T + i] == node;
+  const bool kids = __syncthreads_or(mine);    // uniform
+  if (kids) load(a.draft + (size_t)row * a.V, y);   // in flight during the target's sums
+  stats(x, 0);
+  if (kids) stats(y, 1);
 }
 
 // ---------------------------------------------------------------------------
@@ -577,10 +598,11 @@ hipError_t launch_tree_sampled(const STreePlan& p, const float* target, const fl
   a.B = B; a.T = T; a.V = V; a.nchunks = p.nchunks;
   a.k2 = 1.4426950408889634 / (double)temperature;
   a.k2f = (float)a.k2;
-  stree_stats_kernel<<<dim3(p.nchunks, B * T, 2), kSTThreads, 0, st>>>(a);
+  const bool vec = V % 4 == 0 && ((uintptr_t)target | (uintptr_t)draft) % 16 == 0;
+  if (vec) stree_stats_kernel<true><<<dim3(p.nchunks, B * T), kSTThreads, 0, st>>>(a);
+  else stree_stats_kernel<false><<<dim3(p.nchunks, B * T), kSTThreads, 0, st>>>(a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const bool vec = V % 4 == 0 && ((uintptr_t)target | (uintptr_t)draft) % 16 == 0;
   const dim3 grid(B), block(kSTThreads);
   if (V <= kSTThreads * 16) {
     if (vec) stree_walk_kernel<16, true><<<grid, block, 0, st>>>(a);
