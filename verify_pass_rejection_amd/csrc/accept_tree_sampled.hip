@@ -14,19 +14,19 @@
 //  stree_stats — the whole chip, once over the logits: per 8192-logit chunk
 //                of every target row, and of the draft row of every node with
 //                children, the maximum and Σ 2^((z − max)·log2e/τ);
-//  stree_walk  — one 512-thread block per sequence.  It merges the chunk
-//                statistics of every node and gathers, for every node, p and
-//                q of its parent at its own token, so a ratio test is a few
-//                LDS reads.  A node's rows are read only when a rejection
+//  stree_walk  — one block per sequence (1024 threads for V <= 32768, else
+//                512).  It merges the chunk statistics of every node and
+//                gathers, for every node, p and q of its parent at its own
+//                token, so a ratio test is a few LDS reads.  A node's rows are read only when a rejection
 //                there needs the residual mass, or for the final draw: after j
 //                rejections the residual is (p − c_j q)+ / Z_j, with c_0 = 0,
 //                Z_0 = 1, c_{j+1} = c_j + Z_j and Z_{j+1} = Σ_v (p(v) −
 //                c_{j+1} q(v))+ (one pass per rejection).  For V <= 32768 the
 //                rows, once read, stay on chip while the node is visited: the
-//                target row in registers (up to 64 tokens per thread), the
+//                target row in registers (up to 32 tokens per thread), the
 //                draft row in LDS, thread t holding the float4 groups t,
-//                t + 512, ... (coalesced loads).  The draw then takes the
-//                block totals of the 2048-token segments to find the segment
+//                t + 1024, ... (coalesced loads).  The draw then takes the
+//                block totals of the 4096-token segments to find the segment
 //                holding the crossing, one block scan inside it to find the
 //                thread, and that thread's four tokens to find the token.
 //                For larger V the rows are streamed: each thread sums a
@@ -73,8 +73,9 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 // no swizzle; with stride 0 a read past num_records returns 0.
 constexpr int kBufferWord3 = 0x00020000;
 
-constexpr int kSTThreads = 512;
+constexpr int kSTThreads = 512;                // statistics; the streaming walk
 constexpr int kSTWaves = kSTThreads / kWave;
+constexpr int kSTWalkCached = 1024;            // the walk with rows on chip (V <= 32768)
 constexpr int kSTChunk = 8192;                 // logits per statistics block
 
 // 2^a for a <= 0 (0 below the double range, or for z = -inf); branch-free.
@@ -102,6 +103,7 @@ __device__ __forceinline__ float e_bulk(float z, float m, float k2f) {
 }
 
 // Block reductions: fixed order, the same result in every thread.
+template <int NW>
 __device__ __forceinline__ double block_sum(double x, double* red) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o);
@@ -110,9 +112,10 @@ __device__ __forceinline__ double block_sum(double x, double* red) {
   __syncthreads();
   double s = 0.0;
 #pragma unroll
-  for (int w = 0; w < kSTWaves; ++w) s += red[w];
+  for (int w = 0; w < NW; ++w) s += red[w];
   return s;
 }
+template <int NW>
 __device__ __forceinline__ float block_max(float x, float* redf) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) x = fmaxf(x, __shfl_xor(x, o));
@@ -121,9 +124,10 @@ __device__ __forceinline__ float block_max(float x, float* redf) {
   __syncthreads();
   float m = redf[0];
 #pragma unroll
-  for (int w = 1; w < kSTWaves; ++w) m = fmaxf(m, redf[w]);
+  for (int w = 1; w < NW; ++w) m = fmaxf(m, redf[w]);
   return m;
 }
+template <int NW>
 __device__ __forceinline__ int block_min(int x, int* redi) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) x = min(x, __shfl_xor(x, o));
@@ -132,7 +136,7 @@ __device__ __forceinline__ int block_min(int x, int* redi) {
   __syncthreads();
   int m = redi[0];
 #pragma unroll
-  for (int w = 1; w < kSTWaves; ++w) m = min(m, redi[w]);
+  for (int w = 1; w < NW; ++w) m = min(m, redi[w]);
   return m;
 }
 
@@ -190,7 +194,7 @@ __global__ __launch_bounds__(kSTThreads) void stree_stats_kernel(STreeArgs a) {
     float mx = x[0];
 #pragma unroll
     for (int i = 1; i < PER; ++i) mx = fmaxf(mx, x[i]);
-    mx = block_max(mx, redf);
+    mx = block_max<kSTWaves>(mx, redf);
     double s = 0.0;
     if (mx != -__builtin_huge_valf()) {
 #pragma unroll
@@ -198,7 +202,7 @@ __global__ __launch_bounds__(kSTThreads) void stree_stats_kernel(STreeArgs a) {
         s += (double)((e_bulk(x[i], mx, a.k2f) + e_bulk(x[i + 1], mx, a.k2f)) +
                       (e_bulk(x[i + 2], mx, a.k2f) + e_bulk(x[i + 3], mx, a.k2f)));
     }
-    s = block_sum(s, red);
+    s = block_sum<kSTWaves>(s, red);
     if (threadIdx.x == 0) {
       const size_t o = ((size_t)kind * a.B * a.T + row) * a.nchunks + ch;
       a.part_m[o] = mx;
@@ -216,25 +220,30 @@ __global__ __launch_bounds__(kSTThreads) void stree_stats_kernel(STreeArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// stree_walk.  CH > 0: V <= 512·CH, a visited node's rows are read once,
-// one row at a time with every load in flight (buffer loads; 16 bytes each
-// when VEC), into registers (target) and LDS (draft: element i of this
-// thread at lq[i·512 + tid], conflict-free); element i = 4k + e is token
-// 4·(tid + 512k) + e.  CH = 0: any V, every pass streams the rows from memory.
+// stree_walk, NT threads.  CH > 0: V <= NT·CH, a visited node's rows are read
+// once, one row at a time with every load in flight (buffer loads; 16 bytes
+// each when VEC), into registers (target) and LDS (draft: element i of this
+// thread at lq[i·NT + tid], conflict-free); element i = 4k + e is token
+// 4·(tid + NT·k) + e.  CH = 0: any V, every pass streams the rows from memory.
+// With the rows on chip, 1024 threads (32 tokens each at V = 32768) halve
+// each thread's share of the residual passes, the draw's sums and the
+// exponentials against 512 threads (64 tokens each): call 57.4 -> 55.3 us
+// (eagle2 tree), 95.1 -> 91.5 us (medusa tree).
 // ---------------------------------------------------------------------------
-template <int CH, bool VEC>
-__global__ __launch_bounds__(kSTThreads) void stree_walk_kernel(STreeArgs a) {
+template <int CH, bool VEC, int NT>
+__global__ __launch_bounds__(NT) void stree_walk_kernel(STreeArgs a) {
+  constexpr int NW = NT / kWave;
   constexpr bool CACHED = CH > 0;
   __shared__ int spar[64], stok[64], spath[65], shas[64];
   __shared__ float sua[64];
   __shared__ float nm_p[64], nm_q[64];       // every node's row maxima
   __shared__ double ni_p[64], ni_q[64];      // and 1 / Σ e
   __shared__ double ge_p[64], ge_q[64];      // e of node i's token in its parent's rows
-  __shared__ float lq[CACHED ? CH * kSTThreads : 1];
-  __shared__ double red2[CACHED ? (CH / 4) * kSTWaves : 1];   // segment totals per wave
+  __shared__ float lq[CACHED ? CH * NT : 1];
+  __shared__ double red2[CACHED ? (CH / 4) * NW : 1];   // segment totals per wave
   __shared__ double segS[CACHED ? CH / 4 : 1];                 // and per block
-  __shared__ double red[kSTWaves];
-  __shared__ int redi[kSTWaves];
+  __shared__ double red[NW];
+  __shared__ int redi[NW];
 
   const int b = blockIdx.x, tid = threadIdx.x, lane = tid & 63;
   const int T = a.T, V = a.V;
@@ -287,15 +296,15 @@ __global__ __launch_bounds__(kSTThreads) void stree_walk_kernel(STreeArgs a) {
   const bool my_ok = lane >= 1 && lane < T && my_par >= 0 && my_par < lane;
 
   // Streaming: this thread's tokens j0 .. j1 - 1 (ascending, contiguous).
-  const int chs = (V + kSTThreads - 1) / kSTThreads;
+  const int chs = (V + NT - 1) / NT;
   const int j0 = min(V, tid * chs), j1 = min(V, j0 + chs);
-  // Cached: element i = 4k + e of this thread is token 4·(tid + 512k) + e, so
+  // Cached: element i = 4k + e of this thread is token 4·(tid + NT·k) + e, so
   // that a wave's float4 loads cover 1 KB of consecutive tokens; segment k
-  // (elements 4k .. 4k + 3 of every thread) is tokens 2048k .. 2048k + 2047.
-  auto tok = [&](int i) -> int { return 4 * (tid + kSTThreads * (i >> 2)) + (i & 3); };
+  // (elements 4k .. 4k + 3 of every thread) is tokens 4·NT·k .. 4·NT·(k+1) − 1.
+  auto tok = [&](int i) -> int { return 4 * (tid + NT * (i >> 2)) + (i & 3); };
 
   float rp[CACHED ? CH : 1];
-  auto q_at = [&](int i) -> float& { return lq[i * kSTThreads + tid]; };
+  auto q_at = [&](int i) -> float& { return lq[i * NT + tid]; };
   int n = 0, depth = 0;
   if (tid == 0) spath[0] = 0;
   double c = 0.0, Z = 1.0;
@@ -320,7 +329,7 @@ __global__ __launch_bounds__(kSTThreads) void stree_walk_kernel(STreeArgs a) {
       const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc(
           (void*)zq, (short)0, V * (int)sizeof(float), kBufferWord3);
       auto load4 = [&](__amdgpu_buffer_rsrc_t r, int k, float* d) __attribute__((always_inline)) {
-        const int ofs = kSTThreads * 16 * k;
+        const int ofs = NT * 16 * k;
         if constexpr (VEC) {                      // V % 4 == 0: a group is wholly in or out
           // cast the whole vector: a bit cast of one element of it reads element 0
           const f32x4_t x = __builtin_bit_cast(
@@ -402,9 +411,9 @@ __global__ __launch_bounds__(kSTThreads) void stree_walk_kernel(STreeArgs a) {
         for (int i = 0; i < CH; i += 4)
           s += (double)((res_c(i) + res_c(i + 1)) + (res_c(i + 2) + res_c(i + 3)));
       } else {
-        for (int v = tid; v < V; v += kSTThreads) s += res_s(v);
+        for (int v = tid; v < V; v += NT) s += res_s(v);
       }
-      Z = block_sum(s, red);
+      Z = block_sum<NW>(s, red);
       if (!(Z > 0.0)) { c = 0.0; Z = 1.0; }    // an empty residual falls back to p
     }
     if (kept < 0) break;
@@ -423,7 +432,7 @@ __global__ __launch_bounds__(kSTThreads) void stree_walk_kernel(STreeArgs a) {
   // c = 0 (p itself) or not: one wave-uniform branch for the whole draw
   const bool pure = __builtin_amdgcn_readfirstlane((int)(c == 0.0)) != 0;
 
-  // Cached rows: the block totals of the 2048-token segments locate the
+  // Cached rows: the block totals of the 4·NT-token segments locate the
   // segment holding the crossing; one block scan inside it locates the
   // thread, and that thread's four tokens the token.
   auto draw_cached = [&](auto pure_tag) -> int {
@@ -461,7 +470,7 @@ __global__ __launch_bounds__(kSTThreads) void stree_walk_kernel(STreeArgs a) {
     if (tid < K) {                               // segment totals: the waves in order
       double t = 0.0;
 #pragma unroll
-      for (int w8 = 0; w8 < kSTWaves; ++w8) t += red2[w8 * K + tid];
+      for (int w8 = 0; w8 < NW; ++w8) t += red2[w8 * K + tid];
       segS[tid] = t;
     }
     __syncthreads();
@@ -510,12 +519,12 @@ __global__ __launch_bounds__(kSTThreads) void stree_walk_kernel(STreeArgs a) {
         if (wi > 0.0) last = tok(4 * k + e);
       }
     }
-    int y = block_min(cand, redi);
+    int y = block_min<NW>(cand, redi);
     // Rounding can leave the scan's end of segment ks at or below thr although
     // the segment totals put the crossing inside it: then it is the segment's
     // last token with positive weight.
     if (y >= V) {
-      const int lastpos = -block_min(-last, redi);
+      const int lastpos = -block_min<NW>(-last, redi);
       y = lastpos >= 0 ? lastpos : V;
     }
     return y;
@@ -546,7 +555,7 @@ __global__ __launch_bounds__(kSTThreads) void stree_walk_kernel(STreeArgs a) {
     for (int v = 0; v < (tid >> 6); ++v) base += red[v];
     double total = 0.0;
 #pragma unroll
-    for (int v = 0; v < kSTWaves; ++v) total += red[v];
+    for (int v = 0; v < NW; ++v) total += red[v];
     ex += base;
     const double thr = u * total;
     // this chunk's first token with positive weight whose running mass passes thr
@@ -557,7 +566,7 @@ __global__ __launch_bounds__(kSTThreads) void stree_walk_kernel(STreeArgs a) {
       run += wi;
       if (wi > 0.0 && run > thr) { cand = v; break; }
     }
-    return block_min(cand, redi);
+    return block_min<NW>(cand, redi);
   };
 
   int y;
@@ -566,7 +575,7 @@ __global__ __launch_bounds__(kSTThreads) void stree_walk_kernel(STreeArgs a) {
   if (y >= V) y = V - 1;                      // nothing to draw (a zero total)
 
   __syncthreads();
-  for (int i = tid; i < T; i += kSTThreads) {
+  for (int i = tid; i < T; i += NT) {
     const size_t o = (size_t)b * T + i;
     a.path[o] = i <= depth ? spath[i] : -1;
     a.out[o] = i < depth ? stok[spath[i + 1]] : (i == depth ? y : -1);
@@ -603,18 +612,16 @@ hipError_t launch_tree_sampled(const STreePlan& p, const float* target, const fl
   else stree_stats_kernel<false><<<dim3(p.nchunks, B * T), kSTThreads, 0, st>>>(a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const dim3 grid(B), block(kSTThreads);
-  if (V <= kSTThreads * 16) {
-    if (vec) stree_walk_kernel<16, true><<<grid, block, 0, st>>>(a);
-    else stree_walk_kernel<16, false><<<grid, block, 0, st>>>(a);
-  } else if (V <= kSTThreads * 32) {
-    if (vec) stree_walk_kernel<32, true><<<grid, block, 0, st>>>(a);
-    else stree_walk_kernel<32, false><<<grid, block, 0, st>>>(a);
-  } else if (V <= kSTThreads * 64) {
-    if (vec) stree_walk_kernel<64, true><<<grid, block, 0, st>>>(a);
-    else stree_walk_kernel<64, false><<<grid, block, 0, st>>>(a);
+  const dim3 grid(B);
+  constexpr int NT = kSTWalkCached;
+  if (V <= NT * 16) {
+    if (vec) stree_walk_kernel<16, true, NT><<<grid, NT, 0, st>>>(a);
+    else stree_walk_kernel<16, false, NT><<<grid, NT, 0, st>>>(a);
+  } else if (V <= NT * 32) {
+    if (vec) stree_walk_kernel<32, true, NT><<<grid, NT, 0, st>>>(a);
+    else stree_walk_kernel<32, false, NT><<<grid, NT, 0, st>>>(a);
   } else {
-    stree_walk_kernel<0, false><<<grid, block, 0, st>>>(a);
+    stree_walk_kernel<0, false, kSTThreads><<<grid, kSTThreads, 0, st>>>(a);
   }
   return hipGetLastError();
 }
