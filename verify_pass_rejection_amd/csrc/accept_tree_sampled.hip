@@ -328,37 +328,53 @@ __global__ __launch_bounds__(NT) void stree_walk_kernel(STreeArgs a) {
           (void*)zt, (short)0, V * (int)sizeof(float), kBufferWord3);
       const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc(
           (void*)zq, (short)0, V * (int)sizeof(float), kBufferWord3);
-      auto load4 = [&](__amdgpu_buffer_rsrc_t r, int k, float* d) __attribute__((always_inline)) {
-        const int ofs = NT * 16 * k;
+      // A whole row into d: every load issued before the first use.  With 16-
+      // byte loads the loaded groups pass through one empty asm statement that
+      // takes them all, so the compiler cannot interleave a group's use with the
+      // next group's load (at the 128-register limit it did, leaving one load in
+      // flight at a time).
+      auto load_row = [&](__amdgpu_buffer_rsrc_t r, float (&d)[CH]) __attribute__((always_inline)) {
         if constexpr (VEC) {                      // V % 4 == 0: a group is wholly in or out
-          // cast the whole vector: a bit cast of one element of it reads element 0
-          const f32x4_t x = __builtin_bit_cast(
-              f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, 16 * tid, ofs, 0));
+          f32x4_t x[CH / 4];
 #pragma unroll
-          for (int e = 0; e < 4; ++e) d[e] = x[e];
+          for (int k = 0; k < CH / 4; ++k)
+            // cast the whole vector: a bit cast of one element of it reads element 0
+            x[k] = __builtin_bit_cast(
+                f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, 16 * tid, NT * 16 * k, 0));
+          static_assert(CH == 16 || CH == 32, "row groups per thread");
+          if constexpr (CH == 16) {
+            asm volatile("" : "+v"(x[0]), "+v"(x[1]), "+v"(x[2]), "+v"(x[3]));
+          } else {
+            asm volatile("" : "+v"(x[0]), "+v"(x[1]), "+v"(x[2]), "+v"(x[3]), "+v"(x[4]),
+                         "+v"(x[5]), "+v"(x[6]), "+v"(x[7]));
+          }
+#pragma unroll
+          for (int k = 0; k < CH / 4; ++k)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) d[4 * k + e] = x[k][e];
         } else {
 #pragma unroll
-          for (int e = 0; e < 4; ++e)
-            d[e] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
-                                                 r, 16 * tid + 4 * e, ofs, 0));
+          for (int k = 0; k < CH / 4; ++k)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              d[4 * k + e] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                                           r, 16 * tid + 4 * e, NT * 16 * k, 0));
         }
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-          if (tok(4 * k + e) >= V) d[e] = -__builtin_huge_valf();
+        for (int i = 0; i < CH; ++i)
+          if (tok(i) >= V) d[i] = -__builtin_huge_valf();
       };
       // One row at a time, all of its loads in flight: with both rows' loads
       // outstanding together the compiler ran out of registers and waited for
       // each draft-row load before issuing the next (walk 38.9 -> 46.7 us on
-      // the eagle2 tree).  The draft row's e values are formed in registers
-      // and stored to LDS once.
-#pragma unroll
-      for (int k = 0; k < CH / 4; ++k) load4(rt, k, rp + 4 * k);
+      // the eagle2 tree, 64 tokens per thread).  The draft row's e values are
+      // formed in registers and stored to LDS once.
+      load_row(rt, rp);
 #pragma unroll
       for (int i = 0; i < CH; ++i) rp[i] = e_bulk(rp[i], mp, a.k2f);
       if (both) {
         float y[CH];
-#pragma unroll
-        for (int k = 0; k < CH / 4; ++k) load4(rq, k, y + 4 * k);
+        load_row(rq, y);
 #pragma unroll
         for (int i = 0; i < CH; ++i) q_at(i) = e_bulk(y[i], mq, a.k2f);
       }
