@@ -98,22 +98,46 @@ __global__ __launch_bounds__(kArgThreads) void tree_argmax_kernel(TreeArgs a) {
   }
 }
 
+// Rows of up to kWalkChunks chunks (V <= 65536) are merged from straight-line
+// loads; a loop over the chunks waited for each chunk's pair of loads in turn.
+constexpr int kWalkChunks = 8;
+
 __global__ __launch_bounds__(64) void tree_walk_kernel(TreeArgs a) {
   __shared__ int choice[64], par[64], tok[64], path_nodes[64];
   __shared__ int s_best, s_depth;
   const int b = blockIdx.x, i = threadIdx.x, T = a.T;
   if (i < T) {
     const size_t row = (size_t)b * T + i;
-    float bv = a.part_val[row * a.nchunks];
-    int bi = a.part_idx[row * a.nchunks];
-    for (int c = 1; c < a.nchunks; ++c) {
-      const float v = a.part_val[row * a.nchunks + c];
-      const int j = a.part_idx[row * a.nchunks + c];
-      if (better(v, j, bv, bi)) { bv = v; bi = j; }
+    const int pa = a.parents[row], tk = a.tokens[row];
+    const float* pv = a.part_val + row * a.nchunks;
+    const int* pi = a.part_idx + row * a.nchunks;
+    float bv;
+    int bi;
+    if (a.nchunks <= kWalkChunks) {
+      // every load issued at once: chunks past the last re-read the last one,
+      // which the merge leaves unchanged (equal value and index is not better)
+      float v[kWalkChunks];
+      int j[kWalkChunks];
+#pragma unroll
+      for (int c = 0; c < kWalkChunks; ++c) {
+        const int cc = min(c, a.nchunks - 1);
+        v[c] = pv[cc];
+        j[c] = pi[cc];
+      }
+      bv = v[0];
+      bi = j[0];
+#pragma unroll
+      for (int c = 1; c < kWalkChunks; ++c)
+        if (better(v[c], j[c], bv, bi)) { bv = v[c]; bi = j[c]; }
+    } else {
+      bv = pv[0];
+      bi = pi[0];
+      for (int c = 1; c < a.nchunks; ++c)
+        if (better(pv[c], pi[c], bv, bi)) { bv = pv[c]; bi = pi[c]; }
     }
     choice[i] = bi;
-    par[i] = a.parents[row];
-    tok[i] = a.tokens[row];
+    par[i] = pa;
+    tok[i] = tk;
   }
   __syncthreads();
   // Every node walks up to the root on its own: accepted iff each node on the

@@ -76,6 +76,7 @@ constexpr int kBufferWord3 = 0x00020000;
 constexpr int kSTThreads = 512;                // statistics; the streaming walk
 constexpr int kSTWaves = kSTThreads / kWave;
 constexpr int kSTWalkCached = 1024;            // the walk with rows on chip (V <= 32768)
+constexpr int kSTMergeChunks = 8;              // rows of up to 8 chunks: straight-line merge
 constexpr int kSTChunk = 8192;                 // logits per statistics block
 
 // 2^a for a <= 0 (0 below the double range, or for z = -inf); branch-free.
@@ -248,13 +249,45 @@ __global__ __launch_bounds__(NT) void stree_walk_kernel(STreeArgs a) {
   const int b = blockIdx.x, tid = threadIdx.x, lane = tid & 63;
   const int T = a.T, V = a.V;
   const double k2 = a.k2;
+  // Set-up loads, all issued before the first barrier: the node's parent,
+  // token and uniform (threads 0..T-1); every chunk statistic of the target
+  // row (threads 0..T-1) or draft row (threads 64..64+T-1) of node tid % 64,
+  // the latter also for childless nodes, whose entries are never written and
+  // never used; then the two logits of node tid at its token in its parent's
+  // rows, which wait only for the parent and the token.  (The statistics'
+  // loads go first: a conversion right after the gathers waits for them.)
+  int pa0 = -1, x0 = -1;
+  float ua0 = 0.f;
+  if (tid < T) {
+    pa0 = a.parents[(size_t)b * T + tid];
+    x0 = a.tokens[(size_t)b * T + tid];
+    ua0 = a.u_accept[(size_t)b * T + tid];
+  }
+  float pm[kSTMergeChunks];
+  double ps[kSTMergeChunks];
+  if ((tid & 63) < T && tid < 128 && a.nchunks <= kSTMergeChunks) {
+    const size_t base0 = ((size_t)(tid >> 6) * a.B * T + (size_t)b * T + (tid & 63)) * a.nchunks;
+#pragma unroll
+    for (int c = 0; c < kSTMergeChunks; ++c) {
+      const int cc = min(c, a.nchunks - 1);     // past the last chunk: re-read it, not summed
+      pm[c] = a.part_m[base0 + cc];
+      ps[c] = a.part_s[base0 + cc];
+    }
+  }
+  const bool gth = tid < T && tid >= 1 && pa0 >= 0 && pa0 < tid && x0 >= 0 && x0 < V;
+  float gzt = 0.f, gzq = 0.f;
+  if (gth) {
+    const size_t r = ((size_t)b * T + pa0) * V + x0;
+    gzt = a.target[r];
+    gzq = a.draft[r];
+  }
   if (tid < 64) shas[tid] = 0;
   __syncthreads();
   if (tid < T) {
-    const int pa = a.parents[(size_t)b * T + tid];
+    const int pa = pa0;
     spar[tid] = pa;
-    stok[tid] = a.tokens[(size_t)b * T + tid];
-    sua[tid] = a.u_accept[(size_t)b * T + tid];
+    stok[tid] = x0;
+    sua[tid] = ua0;
     if (tid >= 1 && pa >= 0 && pa < tid) shas[pa] = 1;     // pa has a child
   }
   __syncthreads();
@@ -267,11 +300,20 @@ __global__ __launch_bounds__(NT) void stree_walk_kernel(STreeArgs a) {
     float m = 0.f;
     double inv = 1.0;
     if (has_row) {
-      m = a.part_m[base];
-      for (int c = 1; c < a.nchunks; ++c) m = fmaxf(m, a.part_m[base + c]);
       double s = 0.0;
-      for (int c = 0; c < a.nchunks; ++c)
-        s += a.part_s[base + c] * exp2_split(((double)a.part_m[base + c] - m) * k2);
+      if (a.nchunks <= kSTMergeChunks) {
+        m = pm[0];
+#pragma unroll
+        for (int c = 1; c < kSTMergeChunks; ++c) m = fmaxf(m, pm[c]);
+#pragma unroll
+        for (int c = 0; c < kSTMergeChunks; ++c)
+          if (c < a.nchunks) s += ps[c] * exp2_split(((double)pm[c] - m) * k2);
+      } else {
+        m = a.part_m[base];
+        for (int c = 1; c < a.nchunks; ++c) m = fmaxf(m, a.part_m[base + c]);
+        for (int c = 0; c < a.nchunks; ++c)
+          s += a.part_s[base + c] * exp2_split(((double)a.part_m[base + c] - m) * k2);
+      }
       inv = 1.0 / s;
     }
     if (kind == 0) { nm_p[node] = m; ni_p[node] = inv; }
@@ -280,15 +322,8 @@ __global__ __launch_bounds__(NT) void stree_walk_kernel(STreeArgs a) {
   __syncthreads();
   // e at every node's own token in its parent's target and draft rows.
   if (tid < T) {
-    const int pa = spar[tid], x = stok[tid];
-    double ep = 0.0, eq = 0.0;
-    if (tid >= 1 && pa >= 0 && pa < tid && x >= 0 && x < V) {
-      const size_t r = ((size_t)b * T + pa) * V + x;
-      ep = e_of(a.target[r], nm_p[pa], k2);
-      eq = e_of(a.draft[r], nm_q[pa], k2);
-    }
-    ge_p[tid] = ep;
-    ge_q[tid] = eq;
+    ge_p[tid] = gth ? e_of(gzt, nm_p[pa0], k2) : 0.0;
+    ge_q[tid] = gth ? e_of(gzq, nm_q[pa0], k2) : 0.0;
   }
   __syncthreads();
   // lane i of every wave stands for node i: the same masks in every wave
