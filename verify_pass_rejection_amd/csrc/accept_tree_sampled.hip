@@ -347,6 +347,7 @@ __global__ __launch_bounds__(NT) void stree_walk_kernel(STreeArgs a) {
   const float* zq = nullptr;
   float mp = 0.f, mq = 0.f;
   double ip = 1.0, iq = 1.0;
+  float ipf = 1.f, iqf = 1.f, cf = 0.f;
 
   // Reads the current node's rows as e values (cached path); the draft row
   // only when `both`.
@@ -402,25 +403,25 @@ __global__ __launch_bounds__(NT) void stree_walk_kernel(STreeArgs a) {
       // One row at a time, all of its loads in flight: with both rows' loads
       // outstanding together the compiler ran out of registers and waited for
       // each draft-row load before issuing the next (walk 38.9 -> 46.7 us on
-      // the eagle2 tree, 64 tokens per thread).  The draft row's e values are
-      // formed in registers and stored to LDS once.
+      // the eagle2 tree, 64 tokens per thread).  The rows are kept normalised,
+      // p = e·(1/Z_p) and q = e·(1/Z_q) in float32 (the products every pass
+      // and the draw would otherwise form again); the draft row is formed in
+      // registers and stored to LDS once.
       load_row(rt, rp);
 #pragma unroll
-      for (int i = 0; i < CH; ++i) rp[i] = e_bulk(rp[i], mp, a.k2f);
+      for (int i = 0; i < CH; ++i) rp[i] = e_bulk(rp[i], mp, a.k2f) * ipf;
       if (both) {
         float y[CH];
         load_row(rq, y);
 #pragma unroll
-        for (int i = 0; i < CH; ++i) q_at(i) = e_bulk(y[i], mq, a.k2f);
+        for (int i = 0; i < CH; ++i) q_at(i) = e_bulk(y[i], mq, a.k2f) * iqf;
       }
     }
   };
-  // residual weight (p − c q)+ of element i (cached: float32 terms; q = p
-  // and c = 1 still cancel exactly) or of token v (streaming)
-  float ipf = 1.f, iqf = 1.f, cf = 0.f;
-  auto res_c = [&](int i) -> float {
-    return fmaxf(rp[i] * ipf - cf * (q_at(i) * iqf), 0.f);
-  };
+  // residual weight (p − c q)+ of element i (cached: float32 terms of the
+  // normalised rows; q = p and c = 1 still cancel exactly) or of token v
+  // (streaming)
+  auto res_c = [&](int i) -> float { return fmaxf(rp[i] - cf * q_at(i), 0.f); };
   auto res_s = [&](int v) -> double {
     return fmax((double)e_bulk(zt[v], mp, a.k2f) * ip -
                 c * ((double)e_bulk(zq[v], mq, a.k2f) * iq), 0.0);
@@ -489,7 +490,13 @@ __global__ __launch_bounds__(NT) void stree_walk_kernel(STreeArgs a) {
   auto draw_cached = [&](auto pure_tag) -> int {
     constexpr bool P = decltype(pure_tag)::value;
     constexpr int K = CACHED ? CH / 4 : 1;
-    auto w = [&](int i) -> double { return (double)(P ? rp[i] * ipf : res_c(i)); };
+    // The weights, once, in place of the row (which the walk no longer needs):
+    // the segment sums, the scan and the search below read them from registers.
+    if constexpr (!P) {
+#pragma unroll
+      for (int i = 0; i < CH; ++i) rp[i] = res_c(i);
+    }
+    auto w = [&](int i) -> double { return (double)rp[i]; };
     auto quad = [&](int k) -> double {          // this thread's four tokens of segment k
       return ((w(4 * k) + w(4 * k + 1)) + w(4 * k + 2)) + w(4 * k + 3);
     };
