@@ -223,9 +223,9 @@ __global__ __launch_bounds__(kSTThreads) void stree_stats_kernel(STreeArgs a) {
 // ---------------------------------------------------------------------------
 // stree_walk, NT threads.  CH > 0: V <= NT·CH, a visited node's rows are read
 // once, one row at a time with every load in flight (buffer loads; 16 bytes
-// each when VEC), into registers (target) and LDS (draft: element i of this
-// thread at lq[i·NT + tid], conflict-free); element i = 4k + e is token
-// 4·(tid + NT·k) + e.  CH = 0: any V, every pass streams the rows from memory.
+// each when VEC), into registers (target) and LDS (draft: group k of this
+// thread, elements 4k .. 4k + 3, at float4 k·NT + tid, read with 16-byte LDS
+// reads); element i = 4k + e is token 4·(tid + NT·k) + e.  CH = 0: any V, every pass streams the rows from memory.
 // With the rows on chip, 1024 threads (32 tokens each at V = 32768) halve
 // each thread's share of the residual passes, the draw's sums and the
 // exponentials against 512 threads (64 tokens each): call 57.4 -> 55.3 us
@@ -240,7 +240,7 @@ __global__ __launch_bounds__(NT) void stree_walk_kernel(STreeArgs a) {
   __shared__ float nm_p[64], nm_q[64];       // every node's row maxima
   __shared__ double ni_p[64], ni_q[64];      // and 1 / Σ e
   __shared__ double ge_p[64], ge_q[64];      // e of node i's token in its parent's rows
-  __shared__ float lq[CACHED ? CH * NT : 1];
+  __shared__ __attribute__((aligned(16))) float lq[CACHED ? CH * NT : 4];
   __shared__ double red2[CACHED ? (CH / 4) * NW : 1];   // segment totals per wave
   __shared__ double segS[CACHED ? CH / 4 : 1];                 // and per block
   __shared__ double red[NW];
@@ -339,7 +339,11 @@ __global__ __launch_bounds__(NT) void stree_walk_kernel(STreeArgs a) {
   auto tok = [&](int i) -> int { return 4 * (tid + NT * (i >> 2)) + (i & 3); };
 
   float rp[CACHED ? CH : 1];
-  auto q_at = [&](int i) -> float& { return lq[i * NT + tid]; };
+  // The draft row in LDS: group k (elements 4k .. 4k + 3) of this thread at
+  // float4 k·NT + tid, so a wave's groups are 1 KB contiguous, as one
+  // direct-to-LDS load writes them, and are read with 16-byte LDS reads.
+  typedef __attribute__((address_space(3))) f32x4_t lds_f4;
+  auto q4 = [&](int k) -> lds_f4& { return ((lds_f4*)lq)[k * NT + tid]; };
   int n = 0, depth = 0;
   if (tid == 0) spath[0] = 0;
   double c = 0.0, Z = 1.0;
@@ -414,14 +418,24 @@ __global__ __launch_bounds__(NT) void stree_walk_kernel(STreeArgs a) {
         float y[CH];
         load_row(rq, y);
 #pragma unroll
-        for (int i = 0; i < CH; ++i) q_at(i) = e_bulk(y[i], mq, a.k2f) * iqf;
+        for (int k = 0; k < CH / 4; ++k) {
+          f32x4_t q;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) q[e] = e_bulk(y[4 * k + e], mq, a.k2f) * iqf;
+          q4(k) = q;
+        }
       }
     }
   };
   // residual weight (p − c q)+ of element i (cached: float32 terms of the
   // normalised rows; q = p and c = 1 still cancel exactly) or of token v
   // (streaming)
-  auto res_c = [&](int i) -> float { return fmaxf(rp[i] - cf * q_at(i), 0.f); };
+  // the four weights of group k (cached path)
+  auto res4 = [&](int k, float (&r)[4]) {
+    const f32x4_t q = q4(k);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) r[e] = fmaxf(rp[4 * k + e] - cf * q[e], 0.f);
+  };
   auto res_s = [&](int v) -> double {
     return fmax((double)e_bulk(zt[v], mp, a.k2f) * ip -
                 c * ((double)e_bulk(zq[v], mq, a.k2f) * iq), 0.0);
@@ -460,8 +474,11 @@ __global__ __launch_bounds__(NT) void stree_walk_kernel(STreeArgs a) {
         cf = (float)c;
         // groups of four terms in float32, groups in float64
 #pragma unroll
-        for (int i = 0; i < CH; i += 4)
-          s += (double)((res_c(i) + res_c(i + 1)) + (res_c(i + 2) + res_c(i + 3)));
+        for (int k = 0; k < CH / 4; ++k) {
+          float r[4];
+          res4(k, r);
+          s += (double)((r[0] + r[1]) + (r[2] + r[3]));
+        }
       } else {
         for (int v = tid; v < V; v += NT) s += res_s(v);
       }
@@ -494,7 +511,12 @@ __global__ __launch_bounds__(NT) void stree_walk_kernel(STreeArgs a) {
     // the segment sums, the scan and the search below read them from registers.
     if constexpr (!P) {
 #pragma unroll
-      for (int i = 0; i < CH; ++i) rp[i] = res_c(i);
+      for (int k = 0; k < CH / 4; ++k) {
+        float r[4];
+        res4(k, r);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) rp[4 * k + e] = r[e];
+      }
     }
     auto w = [&](int i) -> double { return (double)rp[i]; };
     auto quad = [&](int k) -> double {          // this thread's four tokens of segment k
