@@ -103,11 +103,51 @@ __device__ __forceinline__ float e_bulk(float z, float m, float k2f) {
   return __builtin_amdgcn_exp2f((z - m) * k2f);
 }
 
+// Lane exchanges without LDS.  dpp_d<C>: each lane takes the double of the
+// lane that DPP control C names within its row of 16 lanes (quad_perm
+// [1,0,3,2] = 0xB1: lane ^ 1; [2,3,0,1] = 0x4E: lane ^ 2; row_half_mirror =
+// 0x141: lane ^ 7 within 8; row_mirror = 0x140: lane ^ 15; row_ror:8 = 0x128:
+// lane ^ 8).
+template <int C>
+__device__ __forceinline__ double dpp_d(double x) {
+  const uint64_t u = __builtin_bit_cast(uint64_t, x);
+  const uint32_t lo = __builtin_amdgcn_mov_dpp((int)(uint32_t)u, C, 0xf, 0xf, false);
+  const uint32_t hi = __builtin_amdgcn_mov_dpp((int)(uint32_t)(u >> 32), C, 0xf, 0xf, false);
+  return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+}
+// The gfx950 row swaps on a pair of doubles (a, b): permlane16 exchanges rows
+// 1, 3 of a with rows 0, 2 of b; permlane32 the upper half of a with the lower
+// half of b.  The sum of the two results is a[l] + a[l ^ 16] (a[l] + a[l ^ 32])
+// in lanes whose bit 4 (bit 5) is clear, and b[l] + b[l ^ 16] (b[l] + b[l ^ 32])
+// in the others.
+template <bool P32>
+__device__ __forceinline__ double swap_sum(double a, double b) {
+  const uint64_t ua = __builtin_bit_cast(uint64_t, a), ub = __builtin_bit_cast(uint64_t, b);
+  const uint32_t alo = (uint32_t)ua, ahi = (uint32_t)(ua >> 32);
+  const uint32_t blo = (uint32_t)ub, bhi = (uint32_t)(ub >> 32);
+  auto rl = P32 ? __builtin_amdgcn_permlane32_swap(alo, blo, false, false)
+                : __builtin_amdgcn_permlane16_swap(alo, blo, false, false);
+  auto rh = P32 ? __builtin_amdgcn_permlane32_swap(ahi, bhi, false, false)
+                : __builtin_amdgcn_permlane16_swap(ahi, bhi, false, false);
+  const double x = __builtin_bit_cast(double, ((uint64_t)(uint32_t)rh[0] << 32) | (uint32_t)rl[0]);
+  const double y = __builtin_bit_cast(double, ((uint64_t)(uint32_t)rh[1] << 32) | (uint32_t)rl[1]);
+  return x + y;
+}
+// Sum over the wave, the same value in every lane (every step adds a pair of
+// lanes' values, which both lanes of the pair then hold).
+__device__ __forceinline__ double wave_sum(double x) {
+  x += dpp_d<0xB1>(x);
+  x += dpp_d<0x4E>(x);
+  x += dpp_d<0x141>(x);
+  x += dpp_d<0x140>(x);
+  x = swap_sum<false>(x, x);
+  return swap_sum<true>(x, x);
+}
+
 // Block reductions: fixed order, the same result in every thread.
 template <int NW>
 __device__ __forceinline__ double block_sum(double x, double* red) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o);
+  x = wave_sum(x);
   __syncthreads();                       // red is free again
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = x;
   __syncthreads();
@@ -524,27 +564,32 @@ __global__ __launch_bounds__(NT) void stree_walk_kernel(STreeArgs a) {
     };
     // The wave's total of every segment: K sums per lane, halved at each step
     // (a lane keeps half of the segments and adds its partner's share of
-    // them), then a butterfly over the lanes left holding the same segment:
-    // lane L ends with segment L / (64 / K).
-    constexpr int LOGK = K == 16 ? 4 : K == 8 ? 3 : K == 4 ? 2 : K == 2 ? 1 : 0;
-    static_assert((1 << LOGK) == K && K <= 64, "segments per lane");
+    // them: partners lane ^ 32, lane ^ 16, lane ^ 8), then a sum over the
+    // 64 / K lanes left holding the same segment: lane L ends with segment
+    // L / (64 / K).  Lane exchanges by row swaps and DPP, not LDS.
+    constexpr int LOGK = K == 8 ? 3 : K == 4 ? 2 : K == 2 ? 1 : 0;
+    static_assert((1 << LOGK) == K && K <= 8, "segments per lane");
     launder(rp);
     double v[K];
 #pragma unroll
     for (int k = 0; k < K; ++k) v[k] = quad(k);
+    if constexpr (LOGK >= 1) {
 #pragma unroll
-    for (int st = 0; st < LOGK; ++st) {
-      const int o = 32 >> st, c = K >> st;     // c segments per lane before this step
-      const bool up = (lane & o) != 0;
-#pragma unroll
-      for (int j = 0; j < c / 2; ++j) {
-        const double keep = up ? v[j + c / 2] : v[j];
-        const double send = up ? v[j] : v[j + c / 2];
-        v[j] = keep + __shfl_xor(send, o);
-      }
+      for (int j = 0; j < K / 2; ++j) v[j] = swap_sum<true>(v[j], v[j + K / 2]);
     }
+    if constexpr (LOGK >= 2) {
 #pragma unroll
-    for (int o = 32 >> LOGK; o > 0; o >>= 1) v[0] += __shfl_xor(v[0], o);
+      for (int j = 0; j < K / 4; ++j) v[j] = swap_sum<false>(v[j], v[j + K / 4]);
+    }
+    if constexpr (LOGK >= 3) {
+      const bool up = (lane & 8) != 0;
+      const double keep = up ? v[1] : v[0], send = up ? v[0] : v[1];
+      v[0] = keep + dpp_d<0x128>(send);
+    }
+    if constexpr (64 / K >= 2) v[0] += dpp_d<0xB1>(v[0]);
+    if constexpr (64 / K >= 4) v[0] += dpp_d<0x4E>(v[0]);
+    if constexpr (64 / K >= 8) v[0] += dpp_d<0x141>(v[0]);
+    if constexpr (64 / K >= 16) v[0] += dpp_d<0x140>(v[0]);
     if ((lane & (64 / K - 1)) == 0) red2[(tid >> 6) * K + lane / (64 / K)] = v[0];
     __syncthreads();
     if (tid < K) {                               // segment totals: the waves in order
