@@ -144,6 +144,42 @@ __device__ __forceinline__ double wave_sum(double x) {
   return swap_sum<true>(x, x);
 }
 
+// dpp_d with no source (a lane shifted in from outside its row or the wave,
+// or a row that row mask R leaves out) giving 0.
+template <int C, int R = 0xf>
+__device__ __forceinline__ double dpp_d0(double x) {
+  const uint64_t u = __builtin_bit_cast(uint64_t, x);
+  const uint32_t lo = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)u, C, R, 0xf, true);
+  const uint32_t hi = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)(u >> 32), C, R, 0xf, true);
+  return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+}
+// Inclusive prefix sum over the wave in lane order: shifts by 1, 2, 4 and 8
+// inside each row of 16 (row_shr 0x111..0x118), then row 0's total into row 1
+// and row 2's into row 3 (row_bcast:15, rows 1 and 3), then the total of
+// lanes 0..31 into rows 2 and 3 (row_bcast:31).
+__device__ __forceinline__ double wave_scan(double x) {
+  x += dpp_d0<0x111>(x);
+  x += dpp_d0<0x112>(x);
+  x += dpp_d0<0x114>(x);
+  x += dpp_d0<0x118>(x);
+  x += dpp_d0<0x142, 0xa>(x);
+  x += dpp_d0<0x143, 0xc>(x);
+  return x;
+}
+// The previous lane's value (wave_shr:1), 0 in lane 0.
+__device__ __forceinline__ double wave_prev(double x) { return dpp_d0<0x138>(x); }
+// Minimum over the wave, in every lane.
+__device__ __forceinline__ int wave_min(int x) {
+  x = min(x, __builtin_amdgcn_mov_dpp(x, 0xB1, 0xf, 0xf, false));
+  x = min(x, __builtin_amdgcn_mov_dpp(x, 0x4E, 0xf, 0xf, false));
+  x = min(x, __builtin_amdgcn_mov_dpp(x, 0x141, 0xf, 0xf, false));
+  x = min(x, __builtin_amdgcn_mov_dpp(x, 0x140, 0xf, 0xf, false));
+  auto r = __builtin_amdgcn_permlane16_swap((uint32_t)x, (uint32_t)x, false, false);
+  x = min((int)r[0], (int)r[1]);
+  r = __builtin_amdgcn_permlane32_swap((uint32_t)x, (uint32_t)x, false, false);
+  return min((int)r[0], (int)r[1]);
+}
+
 // Block reductions: fixed order, the same result in every thread.
 template <int NW>
 __device__ __forceinline__ double block_sum(double x, double* red) {
@@ -170,8 +206,7 @@ __device__ __forceinline__ float block_max(float x, float* redf) {
 }
 template <int NW>
 __device__ __forceinline__ int block_min(int x, int* redi) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) x = min(x, __shfl_xor(x, o));
+  x = wave_min(x);
   __syncthreads();
   if ((threadIdx.x & 63) == 0) redi[threadIdx.x >> 6] = x;
   __syncthreads();
@@ -619,14 +654,8 @@ __global__ __launch_bounds__(NT) void stree_walk_kernel(STreeArgs a) {
     for (int k = 0; k < K; ++k)
       if (k == ks) mine = quad(k);
     // exclusive scan of the threads' sums in segment ks: the wave, then the waves
-    double inc = mine;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const double up = __shfl_up(inc, o);
-      if (lane >= o) inc += up;
-    }
-    double ex = __shfl_up(inc, 1);
-    if (lane == 0) ex = 0.0;
+    const double inc = wave_scan(mine);
+    double ex = wave_prev(inc);
     if (lane == 63) red[tid >> 6] = inc;         // red's last readers are behind the barriers above
     __syncthreads();
     for (int w8 = 0; w8 < (tid >> 6); ++w8) ex += red[w8];
@@ -665,14 +694,8 @@ __global__ __launch_bounds__(NT) void stree_walk_kernel(STreeArgs a) {
     };
     double cs = 0.0;
     for (int v = j0; v < j1; ++v) cs += w(v);
-    double inc = cs;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const double y = __shfl_up(inc, o);
-      if (lane >= o) inc += y;
-    }
-    double ex = __shfl_up(inc, 1);
-    if (lane == 0) ex = 0.0;
+    const double inc = wave_scan(cs);
+    double ex = wave_prev(inc);
     __syncthreads();
     if (lane == 63) red[tid >> 6] = inc;
     __syncthreads();
