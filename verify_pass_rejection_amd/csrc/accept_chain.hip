@@ -94,6 +94,23 @@ __device__ __forceinline__ void merge_ms(float& m, float& s, float m2, float s2,
   s = s * fast_exp2((m - mx) * c) + s2 * fast_exp2((m2 - mx) * c);
   m = mx;
 }
+// (max, sum) over the wave, merged in a fixed order: lane pairs inside each
+// row of 16 by DPP, then row pairs and halves by row swaps (lower first).
+__device__ __forceinline__ void wave_merge_ms(float& m, float& s, float c) {
+  merge_ms(m, s, dpp_f<kDppXor1>(m), dpp_f<kDppXor1>(s), c);
+  merge_ms(m, s, dpp_f<kDppXor2>(m), dpp_f<kDppXor2>(s), c);
+  merge_ms(m, s, dpp_f<kDppXor7>(m), dpp_f<kDppXor7>(s), c);
+  merge_ms(m, s, dpp_f<kDppXor15>(m), dpp_f<kDppXor15>(s), c);
+  float m0, m1, s0, s1;
+  row_pair<false>(m, m0, m1);
+  row_pair<false>(s, s0, s1);
+  m = m0; s = s0;
+  merge_ms(m, s, m1, s1, c);
+  row_pair<true>(m, m0, m1);
+  row_pair<true>(s, s0, s1);
+  m = m0; s = s0;
+  merge_ms(m, s, m1, s1, c);
+}
 
 template <int VEC, bool NT>
 __global__ __launch_bounds__(kStatsThreads) void chain_stats_kernel(ChainArgs a) {
@@ -125,11 +142,7 @@ __global__ __launch_bounds__(kStatsThreads) void chain_stats_kernel(ChainArgs a)
 #pragma unroll
     for (int e = 0; e < ITER * VEC; ++e) s += fast_exp2((v[e] - m) * a.c2);
   }
-#pragma unroll
-  for (int off = 1; off < kWave; off <<= 1) {
-    const float m2 = __shfl_xor(m, off), s2 = __shfl_xor(s, off);
-    merge_ms(m, s, m2, s2, a.c2);
-  }
+  wave_merge_ms(m, s, a.c2);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   if (lane == 0) { sm[wave] = m; ss[wave] = s; }
   __syncthreads();
@@ -220,14 +233,8 @@ __device__ __forceinline__ void chunk_scan(const float* w, float* prefix, float*
   local[0] = w[0];
 #pragma unroll
   for (int e = 1; e < kDrawPer; ++e) local[e] = local[e - 1] + w[e];
-  float incl = local[kDrawPer - 1];
-#pragma unroll
-  for (int off = 1; off < kWave; off <<= 1) {
-    const float y = __shfl_up(incl, off);
-    if (lane >= off) incl += y;
-  }
-  float excl = __shfl_up(incl, 1);
-  if (lane == 0) excl = 0.f;
+  const float incl = wave_scan(local[kDrawPer - 1]);
+  const float excl = wave_prev(incl);
   __syncthreads();                               // wave_tot is free again
   if (lane == kWave - 1) wave_tot[wave] = incl;
   __syncthreads();
@@ -266,11 +273,7 @@ __device__ __forceinline__ int chain_decision(const ChainArgs& a, int b, float* 
     const float2* st = a.stats + ((size_t)b * rows + r) * a.nchunks;
     float M = kNegInf, S = 0.f;
     for (int i = lane; i < a.nchunks; i += kWave) merge_ms(M, S, st[i].x, st[i].y, a.c2);
-#pragma unroll
-    for (int off = 1; off < kWave; off <<= 1) {
-      const float m2 = __shfl_xor(M, off), s2 = __shfl_xor(S, off);
-      merge_ms(M, S, m2, s2, a.c2);
-    }
+    wave_merge_ms(M, S, a.c2);
     if (lane == 0) { row_m[r] = M; row_l[r] = log2f(S); }
   }
   __syncthreads();
@@ -339,14 +342,8 @@ __device__ __forceinline__ void chunk_sums(const ChainArgs& a, const DrawRow& r,
     float l = w[0];
 #pragma unroll
     for (int e = 1; e < kDrawPer; ++e) l = l + w[e];
-    float incl = l;
-#pragma unroll
-    for (int off = 1; off < kWave; off <<= 1) {
-      const float y = __shfl_up(incl, off);
-      if (lane >= off) incl += y;
-    }
-    float ex = __shfl_up(incl, 1);
-    if (lane == 0) ex = 0.f;
+    const float incl = wave_scan(l);
+    const float ex = wave_prev(incl);
     last[cc] = l;
     excl[cc] = ex;
     if (lane == kWave - 1) wave_tot[cc * NW + wave] = incl;
@@ -437,7 +434,8 @@ __global__ __launch_bounds__(kDrawThreads) void chain_select_kernel(ChainArgs a)
       // rounding left no crossing: the last chunk with mass
       const int cstar = cross ? __builtin_ctzll(cross) : mass ? 63 - __builtin_clzll(mass) : -1;
       // without a crossing the prefix is the whole total, as in the serial scan
-      const float carry = cross ? __shfl(acc, cstar) : total;
+      const float carry =
+          cross ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(acc), cstar)) : total;
       if (lane == 0) {
         s_total = total;
         s_chunk = cstar;
@@ -508,14 +506,15 @@ __global__ __launch_bounds__(kDrawThreads) void chain_select_kernel(ChainArgs a)
     const uint64_t ballot = __ballot(pick >= 0);
     int src = 0;
     if (ballot) src = last_mass ? 63 - __builtin_clzll(ballot) : __builtin_ctzll(ballot);
-    const int wtok = __shfl(tok, src);
+    const int wtok = __builtin_amdgcn_readlane(tok, src);   // src: wave-uniform
     if (lane == 0) wave_hit[wave] = ballot ? wtok : -1;
     __syncthreads();
     // every wave: the first (or, for the last positive weight, the last) wave
     // with a hit, from one ballot over the wave results
     const int h = lane < kDrawThreads / kWave ? wave_hit[lane] : -1;
     const uint64_t hits = __ballot(h >= 0);
-    if (hits) y = __shfl(h, last_mass ? 63 - __builtin_clzll(hits) : __builtin_ctzll(hits));
+    if (hits)
+      y = __builtin_amdgcn_readlane(h, last_mass ? 63 - __builtin_clzll(hits) : __builtin_ctzll(hits));
   }
 
   // Emit x_0..x_{k-1}, y, then -1.

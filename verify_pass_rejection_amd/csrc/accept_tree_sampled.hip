@@ -103,83 +103,6 @@ __device__ __forceinline__ float e_bulk(float z, float m, float k2f) {
   return __builtin_amdgcn_exp2f((z - m) * k2f);
 }
 
-// Lane exchanges without LDS.  dpp_d<C>: each lane takes the double of the
-// lane that DPP control C names within its row of 16 lanes (quad_perm
-// [1,0,3,2] = 0xB1: lane ^ 1; [2,3,0,1] = 0x4E: lane ^ 2; row_half_mirror =
-// 0x141: lane ^ 7 within 8; row_mirror = 0x140: lane ^ 15; row_ror:8 = 0x128:
-// lane ^ 8).
-template <int C>
-__device__ __forceinline__ double dpp_d(double x) {
-  const uint64_t u = __builtin_bit_cast(uint64_t, x);
-  const uint32_t lo = __builtin_amdgcn_mov_dpp((int)(uint32_t)u, C, 0xf, 0xf, false);
-  const uint32_t hi = __builtin_amdgcn_mov_dpp((int)(uint32_t)(u >> 32), C, 0xf, 0xf, false);
-  return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
-}
-// The gfx950 row swaps on a pair of doubles (a, b): permlane16 exchanges rows
-// 1, 3 of a with rows 0, 2 of b; permlane32 the upper half of a with the lower
-// half of b.  The sum of the two results is a[l] + a[l ^ 16] (a[l] + a[l ^ 32])
-// in lanes whose bit 4 (bit 5) is clear, and b[l] + b[l ^ 16] (b[l] + b[l ^ 32])
-// in the others.
-template <bool P32>
-__device__ __forceinline__ double swap_sum(double a, double b) {
-  const uint64_t ua = __builtin_bit_cast(uint64_t, a), ub = __builtin_bit_cast(uint64_t, b);
-  const uint32_t alo = (uint32_t)ua, ahi = (uint32_t)(ua >> 32);
-  const uint32_t blo = (uint32_t)ub, bhi = (uint32_t)(ub >> 32);
-  auto rl = P32 ? __builtin_amdgcn_permlane32_swap(alo, blo, false, false)
-                : __builtin_amdgcn_permlane16_swap(alo, blo, false, false);
-  auto rh = P32 ? __builtin_amdgcn_permlane32_swap(ahi, bhi, false, false)
-                : __builtin_amdgcn_permlane16_swap(ahi, bhi, false, false);
-  const double x = __builtin_bit_cast(double, ((uint64_t)(uint32_t)rh[0] << 32) | (uint32_t)rl[0]);
-  const double y = __builtin_bit_cast(double, ((uint64_t)(uint32_t)rh[1] << 32) | (uint32_t)rl[1]);
-  return x + y;
-}
-// Sum over the wave, the same value in every lane (every step adds a pair of
-// lanes' values, which both lanes of the pair then hold).
-__device__ __forceinline__ double wave_sum(double x) {
-  x += dpp_d<0xB1>(x);
-  x += dpp_d<0x4E>(x);
-  x += dpp_d<0x141>(x);
-  x += dpp_d<0x140>(x);
-  x = swap_sum<false>(x, x);
-  return swap_sum<true>(x, x);
-}
-
-// dpp_d with no source (a lane shifted in from outside its row or the wave,
-// or a row that row mask R leaves out) giving 0.
-template <int C, int R = 0xf>
-__device__ __forceinline__ double dpp_d0(double x) {
-  const uint64_t u = __builtin_bit_cast(uint64_t, x);
-  const uint32_t lo = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)u, C, R, 0xf, true);
-  const uint32_t hi = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)(u >> 32), C, R, 0xf, true);
-  return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
-}
-// Inclusive prefix sum over the wave in lane order: shifts by 1, 2, 4 and 8
-// inside each row of 16 (row_shr 0x111..0x118), then row 0's total into row 1
-// and row 2's into row 3 (row_bcast:15, rows 1 and 3), then the total of
-// lanes 0..31 into rows 2 and 3 (row_bcast:31).
-__device__ __forceinline__ double wave_scan(double x) {
-  x += dpp_d0<0x111>(x);
-  x += dpp_d0<0x112>(x);
-  x += dpp_d0<0x114>(x);
-  x += dpp_d0<0x118>(x);
-  x += dpp_d0<0x142, 0xa>(x);
-  x += dpp_d0<0x143, 0xc>(x);
-  return x;
-}
-// The previous lane's value (wave_shr:1), 0 in lane 0.
-__device__ __forceinline__ double wave_prev(double x) { return dpp_d0<0x138>(x); }
-// Minimum over the wave, in every lane.
-__device__ __forceinline__ int wave_min(int x) {
-  x = min(x, __builtin_amdgcn_mov_dpp(x, 0xB1, 0xf, 0xf, false));
-  x = min(x, __builtin_amdgcn_mov_dpp(x, 0x4E, 0xf, 0xf, false));
-  x = min(x, __builtin_amdgcn_mov_dpp(x, 0x141, 0xf, 0xf, false));
-  x = min(x, __builtin_amdgcn_mov_dpp(x, 0x140, 0xf, 0xf, false));
-  auto r = __builtin_amdgcn_permlane16_swap((uint32_t)x, (uint32_t)x, false, false);
-  x = min((int)r[0], (int)r[1]);
-  r = __builtin_amdgcn_permlane32_swap((uint32_t)x, (uint32_t)x, false, false);
-  return min((int)r[0], (int)r[1]);
-}
-
 // Block reductions: fixed order, the same result in every thread.
 template <int NW>
 __device__ __forceinline__ double block_sum(double x, double* red) {
@@ -619,12 +542,12 @@ __global__ __launch_bounds__(NT) void stree_walk_kernel(STreeArgs a) {
     if constexpr (LOGK >= 3) {
       const bool up = (lane & 8) != 0;
       const double keep = up ? v[1] : v[0], send = up ? v[0] : v[1];
-      v[0] = keep + dpp_d<0x128>(send);
+      v[0] = keep + dpp_d<kDppXor8>(send);
     }
-    if constexpr (64 / K >= 2) v[0] += dpp_d<0xB1>(v[0]);
-    if constexpr (64 / K >= 4) v[0] += dpp_d<0x4E>(v[0]);
-    if constexpr (64 / K >= 8) v[0] += dpp_d<0x141>(v[0]);
-    if constexpr (64 / K >= 16) v[0] += dpp_d<0x140>(v[0]);
+    if constexpr (64 / K >= 2) v[0] += dpp_d<kDppXor1>(v[0]);
+    if constexpr (64 / K >= 4) v[0] += dpp_d<kDppXor2>(v[0]);
+    if constexpr (64 / K >= 8) v[0] += dpp_d<kDppXor7>(v[0]);
+    if constexpr (64 / K >= 16) v[0] += dpp_d<kDppXor15>(v[0]);
     if ((lane & (64 / K - 1)) == 0) red2[(tid >> 6) * K + lane / (64 / K)] = v[0];
     __syncthreads();
     if (tid < K) {                               // segment totals: the waves in order
