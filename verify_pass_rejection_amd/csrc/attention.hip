@@ -140,19 +140,14 @@ __device__ __forceinline__ void merge_state(float& m, float& l, float m2, float 
 // group keeps its own online-softmax state over its keys; the groups and the
 // waves are merged at the end.
 // ---------------------------------------------------------------------------
-template <int CTRL>
-__device__ __forceinline__ float dpp_f(float v) {
-  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xf, 0xf, false));
-}
-
 // Sum over aligned groups of LPK lanes (LPK in {8, 16, 32}); every lane of a
 // group ends with the same bits (each step adds a commuted pair).
 template <int LPK>
 __device__ __forceinline__ float group_sum(float v) {
-  v += dpp_f<0xB1>(v);     // quad_perm [1,0,3,2]: lane ^ 1
-  v += dpp_f<0x4E>(v);     // quad_perm [2,3,0,1]: lane ^ 2
-  v += dpp_f<0x141>(v);    // row_half_mirror: quad 0 <-> quad 1 of each 8
-  if constexpr (LPK >= 16) v += dpp_f<0x140>(v);   // row_mirror: halves of each 16
+  v += dpp_f<kDppXor1>(v);                           // quad_perm [1,0,3,2]
+  v += dpp_f<kDppXor2>(v);                           // quad_perm [2,3,0,1]
+  v += dpp_f<kDppXor7>(v);                           // row_half_mirror: quads of each 8
+  if constexpr (LPK >= 16) v += dpp_f<kDppXor15>(v); // row_mirror: halves of each 16
   if constexpr (LPK >= 32) v += __shfl_xor(v, 16);
   return v;
 }
