@@ -117,8 +117,7 @@ __device__ __forceinline__ double block_sum(double x, double* red) {
 }
 template <int NW>
 __device__ __forceinline__ float block_max(float x, float* redf) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) x = fmaxf(x, __shfl_xor(x, o));
+  x = wave_max(x);
   __syncthreads();
   if ((threadIdx.x & 63) == 0) redf[threadIdx.x >> 6] = x;
   __syncthreads();

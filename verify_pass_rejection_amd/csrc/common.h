@@ -98,6 +98,18 @@ __device__ __forceinline__ double wave_sum(double x) {
   x = swap_sum<false>(x, x);
   return swap_sum<true>(x, x);
 }
+// Maximum over the wave, in every lane.
+__device__ __forceinline__ float wave_max(float x) {
+  x = fmaxf(x, dpp_f<kDppXor1>(x));
+  x = fmaxf(x, dpp_f<kDppXor2>(x));
+  x = fmaxf(x, dpp_f<kDppXor7>(x));
+  x = fmaxf(x, dpp_f<kDppXor15>(x));
+  float lo, hi;
+  row_pair<false>(x, lo, hi);
+  x = fmaxf(lo, hi);
+  row_pair<true>(x, lo, hi);
+  return fmaxf(lo, hi);
+}
 // Minimum over the wave, in every lane.
 __device__ __forceinline__ int wave_min(int x) {
   x = min(x, __builtin_amdgcn_mov_dpp(x, kDppXor1, 0xf, 0xf, false));
