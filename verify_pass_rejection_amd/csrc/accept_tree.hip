@@ -47,6 +47,24 @@ typedef float f32x4_nt __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ bool better(float v, int i, float bv, int bi) {
   return v > bv || (v == bv && i < bi);
 }
+// The best (value, index) over the wave, in every lane: lane pairs inside
+// each row by DPP, then row pairs and halves by row swaps.
+__device__ __forceinline__ void wave_best(float& bv, int& bi) {
+  auto take = [&](float ov, int oi) { if (better(ov, oi, bv, bi)) { bv = ov; bi = oi; } };
+  take(dpp_f<kDppXor1>(bv), __builtin_amdgcn_mov_dpp(bi, kDppXor1, 0xf, 0xf, false));
+  take(dpp_f<kDppXor2>(bv), __builtin_amdgcn_mov_dpp(bi, kDppXor2, 0xf, 0xf, false));
+  take(dpp_f<kDppXor7>(bv), __builtin_amdgcn_mov_dpp(bi, kDppXor7, 0xf, 0xf, false));
+  take(dpp_f<kDppXor15>(bv), __builtin_amdgcn_mov_dpp(bi, kDppXor15, 0xf, 0xf, false));
+  float vlo, vhi, ilo, ihi;
+  row_pair<false>(bv, vlo, vhi);
+  row_pair<false>(__int_as_float(bi), ilo, ihi);
+  bv = vlo; bi = __float_as_int(ilo);
+  take(vhi, __float_as_int(ihi));
+  row_pair<true>(bv, vlo, vhi);
+  row_pair<true>(__int_as_float(bi), ilo, ihi);
+  bv = vlo; bi = __float_as_int(ilo);
+  take(vhi, __float_as_int(ihi));
+}
 
 template <int VEC>
 __global__ __launch_bounds__(kArgThreads) void tree_argmax_kernel(TreeArgs a) {
@@ -81,12 +99,7 @@ __global__ __launch_bounds__(kArgThreads) void tree_argmax_kernel(TreeArgs a) {
       const int j = begin + (it * kArgThreads + threadIdx.x) * VEC + e;
       if (j < a.V && better(v[it * VEC + e], j, bv, bi)) { bv = v[it * VEC + e]; bi = j; }
     }
-#pragma unroll
-  for (int off = 1; off < kWave; off <<= 1) {
-    const float ov = __shfl_xor(bv, off);
-    const int oi = __shfl_xor(bi, off);
-    if (better(ov, oi, bv, bi)) { bv = ov; bi = oi; }
-  }
+  wave_best(bv, bi);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   if (lane == 0) { sv_[wave] = bv; si_[wave] = bi; }
   __syncthreads();

@@ -148,7 +148,24 @@ __device__ __forceinline__ float group_sum(float v) {
   v += dpp_f<kDppXor2>(v);                           // quad_perm [2,3,0,1]
   v += dpp_f<kDppXor7>(v);                           // row_half_mirror: quads of each 8
   if constexpr (LPK >= 16) v += dpp_f<kDppXor15>(v); // row_mirror: halves of each 16
-  if constexpr (LPK >= 32) v += __shfl_xor(v, 16);
+  if constexpr (LPK >= 32) {                         // row pairs: 32-lane halves
+    float lo, hi;
+    row_pair<false>(v, lo, hi);
+    v = lo + hi;
+  }
+  return v;
+}
+template <int LPK>
+__device__ __forceinline__ float group_max(float v) {
+  v = fmaxf(v, dpp_f<kDppXor1>(v));
+  v = fmaxf(v, dpp_f<kDppXor2>(v));
+  v = fmaxf(v, dpp_f<kDppXor7>(v));
+  if constexpr (LPK >= 16) v = fmaxf(v, dpp_f<kDppXor15>(v));
+  if constexpr (LPK >= 32) {
+    float lo, hi;
+    row_pair<false>(v, lo, hi);
+    v = fmaxf(lo, hi);
+  }
   return v;
 }
 
@@ -835,8 +852,7 @@ __global__ __launch_bounds__(kCombineThreads) void attn_combine_kernel(AttnArgs 
   float mx = kNegInf;
   if (live)
     for (int sp = g; sp < S; sp += GL) mx = fmaxf(mx, a.part_ml[(base + (size_t)sp * a.R) * 2]);
-#pragma unroll
-  for (int off = 1; off < GL; off <<= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+  mx = group_max<GL>(mx);
   // Split weights into LDS and the weighted sum of the row sums.
   float den = 0.f;
   if (live)
@@ -847,8 +863,7 @@ __global__ __launch_bounds__(kCombineThreads) void attn_combine_kernel(AttnArgs 
       wsh[r][sp] = w;
       den = fmaf(w, a.part_ml[pi * 2 + 1], den);
     }
-#pragma unroll
-  for (int off = 1; off < GL; off <<= 1) den += __shfl_xor(den, off);
+  den = group_sum<GL>(den);
   __syncthreads();
   if (!live) return;
   f32x4_t num = {0.f, 0.f, 0.f, 0.f};

@@ -5,6 +5,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace sv {
 
 constexpr int kWave = 64;
@@ -109,6 +111,28 @@ __device__ __forceinline__ float wave_max(float x) {
   x = fmaxf(lo, hi);
   row_pair<true>(x, lo, hi);
   return fmaxf(lo, hi);
+}
+// Maximum of unsigned 64-bit keys over the wave, in every lane.
+__device__ __forceinline__ uint64_t wave_max(uint64_t x) {
+  auto step = [](uint64_t v, uint64_t y) { return y > v ? y : v; };
+  auto dpp = [](uint64_t v, auto c) {
+    constexpr int C = decltype(c)::value;
+    const uint32_t lo = __builtin_amdgcn_mov_dpp((int)(uint32_t)v, C, 0xf, 0xf, false);
+    const uint32_t hi = __builtin_amdgcn_mov_dpp((int)(uint32_t)(v >> 32), C, 0xf, 0xf, false);
+    return ((uint64_t)hi << 32) | lo;
+  };
+  x = step(x, dpp(x, std::integral_constant<int, kDppXor1>{}));
+  x = step(x, dpp(x, std::integral_constant<int, kDppXor2>{}));
+  x = step(x, dpp(x, std::integral_constant<int, kDppXor7>{}));
+  x = step(x, dpp(x, std::integral_constant<int, kDppXor15>{}));
+  auto rl = __builtin_amdgcn_permlane16_swap((uint32_t)x, (uint32_t)x, false, false);
+  auto rh = __builtin_amdgcn_permlane16_swap((uint32_t)(x >> 32), (uint32_t)(x >> 32), false, false);
+  x = step(((uint64_t)(uint32_t)rh[0] << 32) | (uint32_t)rl[0],
+           ((uint64_t)(uint32_t)rh[1] << 32) | (uint32_t)rl[1]);
+  rl = __builtin_amdgcn_permlane32_swap((uint32_t)x, (uint32_t)x, false, false);
+  rh = __builtin_amdgcn_permlane32_swap((uint32_t)(x >> 32), (uint32_t)(x >> 32), false, false);
+  return step(((uint64_t)(uint32_t)rh[0] << 32) | (uint32_t)rl[0],
+              ((uint64_t)(uint32_t)rh[1] << 32) | (uint32_t)rl[1]);
 }
 // Minimum over the wave, in every lane.
 __device__ __forceinline__ int wave_min(int x) {

@@ -94,11 +94,7 @@ __global__ __launch_bounds__(kNgThreads) void ngram_scan_kernel(NgramArgs a) {
     }
   }
   // block maximum of the keys
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    const uint64_t y = __shfl_xor(best, o);
-    best = y > best ? y : best;
-  }
+  best = wave_max(best);
   if ((tid & 63) == 0) red[tid >> 6] = best;
   __syncthreads();
   if (tid == 0) {
@@ -116,11 +112,7 @@ __global__ __launch_bounds__(kWave) void ngram_finalize_kernel(NgramArgs a) {
     const uint64_t k = a.part[(size_t)b * a.tiles + t];
     best = k > best ? k : best;
   }
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    const uint64_t y = __shfl_xor(best, o);
-    best = y > best ? y : best;
-  }
+  best = wave_max(best);
   const int e = best == 0 ? -1 : (int)(uint32_t)best - 1;
   const int n = e < 0 ? 0 : min(a.N, L - 1 - e);
   const int32_t* c = a.ctx + (size_t)b * a.L;
