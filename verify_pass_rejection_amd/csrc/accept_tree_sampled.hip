@@ -63,6 +63,7 @@ struct STreeArgs {
   int32_t* out;            // [B, T]
   float* part_m;           // [2, B*T, nchunks] chunk maxima (target rows, then draft rows)
   double* part_s;          // [2, B*T, nchunks] chunk sums
+  float2* gz;              // [B*T] node i: target and draft logit of its parent at its token
   int B, T, V, nchunks;
   double k2;               // log2(e) / temperature
   float k2f;               // the same, rounded to float32
@@ -151,7 +152,9 @@ __device__ __forceinline__ void launder(float (&r)[N]) {
 // ---------------------------------------------------------------------------
 // stree_stats: block (chunk, row): that chunk of the node's target row and,
 // when the node has children, of its draft row (no other draft row is ever
-// used).  Whether it has children is read (one parent per thread, a block OR)
+// used).  A child whose token falls in the chunk copies its parent's two
+// logits at that token into gz, so that the walk reads them with its other
+// set-up loads instead of gathering them after the parents arrive.  Whether it has children is read (one parent per thread, a block OR)
 // while the target chunk's loads are in flight, and the draft chunk's loads
 // are in flight while the target chunk is summed.  16-byte loads when VEC, with
 // indices clamped into the row, so every load is issued before the first use.
@@ -210,7 +213,13 @@ __global__ __launch_bounds__(kSTThreads) void stree_stats_kernel(STreeArgs a) {
   float x[PER], y[PER];
   load(a.target + (size_t)row * a.V, x);
   const int i = threadIdx.x;
-  const bool mine = i > node && i < a.T && a.parents[(size_t)b * a.T + i] == node;
+  const size_t ci = (size_t)b * a.T + min(i, a.T - 1);
+  const int ipar = a.parents[ci], itok = a.tokens[ci];
+  const bool mine = i > node && i < a.T && ipar == node;
+  if (mine && itok >= begin && itok < end) {
+    const size_t r = (size_t)row * a.V + itok;
+    a.gz[ci] = make_float2(a.target[r], a.draft[r]);
+  }
   const bool kids = __syncthreads_or(mine);    // uniform
   if (kids) load(a.draft + (size_t)row * a.V, y);   // in flight during the target's sums
   stats(x, 0);
@@ -246,19 +255,21 @@ __global__ __launch_bounds__(NT) void stree_walk_kernel(STreeArgs a) {
   const int b = blockIdx.x, tid = threadIdx.x, lane = tid & 63;
   const int T = a.T, V = a.V;
   const double k2 = a.k2;
-  // Set-up loads, all issued before the first barrier: the node's parent,
-  // token and uniform (threads 0..T-1); every chunk statistic of the target
+  // Set-up loads, all issued at once before the first barrier: the node's
+  // parent, token, uniform and the two logits of its parent at its token,
+  // which the statistics pass copied (threads 0..T-1; an entry is written for
+  // exactly the nodes that use it below); every chunk statistic of the target
   // row (threads 0..T-1) or draft row (threads 64..64+T-1) of node tid % 64,
   // the latter also for childless nodes, whose entries are never written and
-  // never used; then the two logits of node tid at its token in its parent's
-  // rows, which wait only for the parent and the token.  (The statistics'
-  // loads go first: a conversion right after the gathers waits for them.)
+  // never used.
   int pa0 = -1, x0 = -1;
   float ua0 = 0.f;
+  float2 gz = make_float2(0.f, 0.f);
   if (tid < T) {
     pa0 = a.parents[(size_t)b * T + tid];
     x0 = a.tokens[(size_t)b * T + tid];
     ua0 = a.u_accept[(size_t)b * T + tid];
+    gz = a.gz[(size_t)b * T + tid];
   }
   float pm[kSTMergeChunks];
   double ps[kSTMergeChunks];
@@ -272,12 +283,6 @@ __global__ __launch_bounds__(NT) void stree_walk_kernel(STreeArgs a) {
     }
   }
   const bool gth = tid < T && tid >= 1 && pa0 >= 0 && pa0 < tid && x0 >= 0 && x0 < V;
-  float gzt = 0.f, gzq = 0.f;
-  if (gth) {
-    const size_t r = ((size_t)b * T + pa0) * V + x0;
-    gzt = a.target[r];
-    gzq = a.draft[r];
-  }
   if (tid < 64) shas[tid] = 0;
   __syncthreads();
   if (tid < T) {
@@ -319,8 +324,8 @@ __global__ __launch_bounds__(NT) void stree_walk_kernel(STreeArgs a) {
   __syncthreads();
   // e at every node's own token in its parent's target and draft rows.
   if (tid < T) {
-    ge_p[tid] = gth ? e_of(gzt, nm_p[pa0], k2) : 0.0;
-    ge_q[tid] = gth ? e_of(gzq, nm_q[pa0], k2) : 0.0;
+    ge_p[tid] = gth ? e_of(gz.x, nm_p[pa0], k2) : 0.0;
+    ge_q[tid] = gth ? e_of(gz.y, nm_q[pa0], k2) : 0.0;
   }
   __syncthreads();
   // lane i of every wave stands for node i: the same masks in every wave
@@ -659,7 +664,8 @@ STreePlan plan_tree_sampled(int B, int T, int V) {
   const size_t parts = (size_t)2 * B * T * p.nchunks;
   p.s_bytes = align256(parts * sizeof(double));
   p.m_bytes = align256(parts * sizeof(float));
-  p.total_bytes = p.s_bytes + p.m_bytes;
+  p.g_bytes = align256((size_t)B * T * sizeof(float2));
+  p.total_bytes = p.s_bytes + p.m_bytes + p.g_bytes;
   return p;
 }
 
@@ -674,6 +680,7 @@ hipError_t launch_tree_sampled(const STreePlan& p, const float* target, const fl
   a.accept_len = accept_len; a.path = path; a.out = out;
   a.part_s = (double*)workspace;
   a.part_m = (float*)((char*)workspace + p.s_bytes);
+  a.gz = (float2*)((char*)workspace + p.s_bytes + p.m_bytes);
   a.B = B; a.T = T; a.V = V; a.nchunks = p.nchunks;
   a.k2 = 1.4426950408889634 / (double)temperature;
   a.k2f = (float)a.k2;

@@ -203,7 +203,7 @@ struct TreePlan {
 
 struct STreePlan {
   int nchunks;     // 8192-logit statistics chunks per row
-  size_t s_bytes, m_bytes, total_bytes;
+  size_t s_bytes, m_bytes, g_bytes, total_bytes;
 };
 
 struct NgramPlan {
