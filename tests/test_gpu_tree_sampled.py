@@ -91,6 +91,22 @@ def test_root_only_leaf_and_edge_inputs():
     compare(I.make_sampled_tree_inputs(w1, dev), label="V=1")
 
 
+def test_tokens_on_statistics_chunk_edges():
+    """Draft tokens at the first and last logit of the 8192-logit statistics
+    chunks: the chunk holding a child's token is the one that records its
+    parent's logits there for the walk."""
+    dev = device()
+    w = I.WORKLOADS["eagle2_tree"].with_(B=6, V=20000, seed=44)
+    d = I.make_sampled_tree_inputs(w, dev)
+    edges = torch.tensor([0, 8191, 8192, 16383, 16384, 19999], dtype=torch.int32)
+    tok = d["tokens"].clone()
+    for b in range(w.B):
+        tok[b, 1:] = edges[(torch.arange(1, w.T) + b) % len(edges)].to(tok.device)
+    d2 = dict(d)
+    d2["tokens"] = tok
+    compare(d2, label="chunk-edge tokens")
+
+
 def test_deterministic_run_twice():
     dev = device()
     d = I.make_sampled_tree_inputs(I.WORKLOADS["medusa70b_tree"].with_(B=8, V=5000), dev)
