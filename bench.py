@@ -82,6 +82,7 @@ class Step:
         self.num = torch.empty(w.B, dtype=torch.int32, device=dev)
         self.tok = torch.empty((w.B, w.T), dtype=torch.int32, device=dev)
         self.path = torch.empty((w.B, w.T), dtype=torch.int32, device=dev)
+        self.new_len = torch.empty(w.B, dtype=torch.int32, device=dev)   # KV commit output
         dt = nat.SPEC_BF16 if w.dtype == "bf16" else nat.SPEC_F32
         self.ws_a = torch.empty(nat.spec_verify_attention_workspace(
             w.B, w.T, w.Hq, w.Hkv, w.D, w.ctx, dt), dtype=torch.uint8, device=dev)
@@ -164,27 +165,35 @@ def time_steps(step, steps: int, warmup: int, flush=None):
                 accept_pct_ms=[pct(acc, q) for q in (0.1, 0.5, 0.9)])
 
 
-def time_commit(step, steps: int):
+def time_commit(step, steps: int, flush=None):
     """spec_commit_kv after the tree acceptance of the last timed step (runs
     last: it rewrites the new positions of K/V in place; repeating it with the
-    same path moves the same rows again, the same work)."""
+    same path moves the same rows again, the same work).  Timed per call with
+    events, flush as for the step: the flush read before each call also keeps
+    the host's launch out of the event pair, as for the other per-call figures
+    (a loop of back-to-back calls measures the Python binding instead)."""
     import torch
     w, nat = step.w, step.nat
+    run = lambda: nat.spec_commit_kv(step.k, step.v, w.ctx, step.num, path=step.path,  # noqa: E731
+                                     new_len=step.new_len)
     for _ in range(3):
-        nat.spec_commit_kv(step.k, step.v, w.ctx, step.num, path=step.path)
+        run()
     torch.cuda.synchronize()
-    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    s.record()
-    for _ in range(steps):
-        nat.spec_commit_kv(step.k, step.v, w.ctx, step.num, path=step.path)
-    e.record()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
+    for i in range(steps):
+        if flush is not None:
+            evict(flush)
+        ev[i][0].record()
+        run()
+        ev[i][1].record()
     torch.cuda.synchronize()
-    us = s.elapsed_time(e) / steps * 1e3
+    ts = [a.elapsed_time(b) * 1e3 for a, b in ev]
+    us = pct(ts, 0.5)
     esize = 2 if w.dtype == "bf16" else 4
     rows = int((step.num.clamp(0, w.T - 1) + 1).sum()) * w.Hkv
     moved = rows * w.D * esize * 2 * 2          # K and V rows, read and written
-    return {"us": round(us, 2), "bytes_moved": moved,
-            "GBps": round(moved / (us * 1e-6) / 1e9, 2),
+    return {"us": round(us, 2), "us_p10_p50_p90": [round(pct(ts, q), 2) for q in (0.1, 0.5, 0.9)],
+            "bytes_moved": moved, "GBps": round(moved / (us * 1e-6) / 1e9, 2),
             "note": "latency-bound: a few hundred KB per call"}
 
 
@@ -510,7 +519,7 @@ def measure_config(name, dev, steps: int, warmup: int, with_alpha: bool):
     if with_alpha and w.kind == "chain":
         out.update(measure_alpha(w, dev, step, max(40, steps), flush))
     if w.kind == "tree":
-        out["kv_commit"] = time_commit(step, steps)
+        out["kv_commit"] = time_commit(step, steps, flush)
         out["sampled_tree_acceptance"] = time_sampled_tree(w, dev, steps, flush)
     del step, flush
     torch.cuda.empty_cache()
