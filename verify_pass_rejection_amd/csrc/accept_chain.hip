@@ -94,13 +94,17 @@ __device__ __forceinline__ void merge_ms(float& m, float& s, float m2, float s2,
   s = s * fast_exp2((m - mx) * c) + s2 * fast_exp2((m2 - mx) * c);
   m = mx;
 }
-// (max, sum) over the wave, merged in a fixed order: lane pairs inside each
-// row of 16 by DPP, then row pairs and halves by row swaps (lower first).
-__device__ __forceinline__ void wave_merge_ms(float& m, float& s, float c) {
+// (max, sum) over each row of 16 lanes, merged in a fixed order by DPP.
+__device__ __forceinline__ void group16_merge_ms(float& m, float& s, float c) {
   merge_ms(m, s, dpp_f<kDppXor1>(m), dpp_f<kDppXor1>(s), c);
   merge_ms(m, s, dpp_f<kDppXor2>(m), dpp_f<kDppXor2>(s), c);
   merge_ms(m, s, dpp_f<kDppXor7>(m), dpp_f<kDppXor7>(s), c);
   merge_ms(m, s, dpp_f<kDppXor15>(m), dpp_f<kDppXor15>(s), c);
+}
+// (max, sum) over the wave: the rows of 16 first, then row pairs and halves
+// by row swaps (lower first).
+__device__ __forceinline__ void wave_merge_ms(float& m, float& s, float c) {
+  group16_merge_ms(m, s, c);
   float m0, m1, s0, s1;
   row_pair<false>(m, m0, m1);
   row_pair<false>(s, s0, s1);
@@ -269,12 +273,26 @@ __device__ __forceinline__ int chain_decision(const ChainArgs& a, int b, float* 
       zq = a.draft[((size_t)b * N + tid) * a.V + x];
     }
   }
-  for (int r = wave; r < rows; r += NT / kWave) {
-    const float2* st = a.stats + ((size_t)b * rows + r) * a.nchunks;
-    float M = kNegInf, S = 0.f;
-    for (int i = lane; i < a.nchunks; i += kWave) merge_ms(M, S, st[i].x, st[i].y, a.c2);
-    wave_merge_ms(M, S, a.c2);
-    if (lane == 0) { row_m[r] = M; row_l[r] = log2f(S); }
+  if (a.nchunks <= 16) {
+    // 16 lanes per row, every row in one pass (up to 64 rows): lanes past the
+    // row's chunks hold (-inf, 0), which every merge step passes through
+    // exactly, so the result is that of a merge over the whole wave
+    const int l16 = tid & 15;
+    for (int r = tid >> 4; r < rows; r += NT / 16) {
+      const float2* st = a.stats + ((size_t)b * rows + r) * a.nchunks;
+      float M = kNegInf, S = 0.f;
+      if (l16 < a.nchunks) merge_ms(M, S, st[l16].x, st[l16].y, a.c2);
+      group16_merge_ms(M, S, a.c2);
+      if (l16 == 0) { row_m[r] = M; row_l[r] = log2f(S); }
+    }
+  } else {
+    for (int r = wave; r < rows; r += NT / kWave) {
+      const float2* st = a.stats + ((size_t)b * rows + r) * a.nchunks;
+      float M = kNegInf, S = 0.f;
+      for (int i = lane; i < a.nchunks; i += kWave) merge_ms(M, S, st[i].x, st[i].y, a.c2);
+      wave_merge_ms(M, S, a.c2);
+      if (lane == 0) { row_m[r] = M; row_l[r] = log2f(S); }
+    }
   }
   __syncthreads();
   // The N <= 63 ratio tests sit in wave 0: k is its first failing lane.
