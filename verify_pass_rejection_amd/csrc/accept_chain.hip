@@ -254,8 +254,9 @@ __device__ __forceinline__ void chunk_scan(const float* w, float* prefix, float*
 
 // The decision of sequence b, taken by a whole block of NT threads: merges the
 // chunk statistics into the row normalisers (row_m: max, row_l: log2 of the
-// sum; one wave per row, lane-strided partial merges then a butterfly, a
-// fixed order), runs the N ratio tests (keep x_i iff u < p_i(x_i)/q_i(x_i))
+// sum; 16 lanes per row when a row has at most 16 chunks, else a wave with
+// lane-strided partial merges, then DPP and row-swap merges in a fixed
+// order), runs the N ratio tests (keep x_i iff u < p_i(x_i)/q_i(x_i))
 // and returns k, the first rejection (N if none), to every thread.
 template <int NT>
 __device__ __forceinline__ int chain_decision(const ChainArgs& a, int b, float* row_m,
