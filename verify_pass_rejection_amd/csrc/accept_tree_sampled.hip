@@ -152,19 +152,21 @@ __device__ __forceinline__ void launder(float (&r)[N]) {
 // ---------------------------------------------------------------------------
 // stree_stats: block (chunk, row): that chunk of the node's target row and,
 // when the node has children, of its draft row (no other draft row is ever
-// used).  A child whose token falls in the chunk copies its parent's two
-// logits at that token into gz, so that the walk reads them with its other
-// set-up loads instead of gathering them after the parents arrive.  Whether it has children is read (one parent per thread, a block OR)
-// while the target chunk's loads are in flight, and the draft chunk's loads
-// are in flight while the target chunk is summed.  16-byte loads when VEC, with
-// indices clamped into the row, so every load is issued before the first use.
-// Ordinary (cached) loads: the walk reads the rows of the visited nodes again
-// right after this pass, and finds them in the last-level cache.
+// used).  Whether it has children is read (one parent per thread, a block OR)
+// while the target chunk's loads are in flight.  The two chunks' maxima are
+// reduced side by side, then their sums, so a node with children costs one
+// pair of barriers per reduction, as a leaf does.  A child whose token falls
+// in the chunk copies its parent's two logits at that token into gz, so that
+// the walk reads them with its other set-up loads instead of gathering them
+// after the parents arrive.  16-byte loads when VEC, with indices clamped into
+// the row, so every load is issued before the first use.  Ordinary (cached)
+// loads: the walk reads the rows of the visited nodes again right after this
+// pass, and finds them in the last-level cache.
 // ---------------------------------------------------------------------------
 template <bool VEC>
 __global__ __launch_bounds__(kSTThreads) void stree_stats_kernel(STreeArgs a) {
-  __shared__ double red[kSTWaves];
-  __shared__ float redf[kSTWaves];
+  __shared__ double red[2 * kSTWaves];
+  __shared__ float redf[2 * kSTWaves];
   const int ch = blockIdx.x, row = blockIdx.y;
   const int b = row / a.T, node = row % a.T;
   const int begin = ch * kSTChunk, end = min(a.V, begin + kSTChunk);
@@ -191,11 +193,13 @@ __global__ __launch_bounds__(kSTThreads) void stree_stats_kernel(STreeArgs a) {
   // roundings), groups in float64; a chunk of -inf logits (a masked
   // vocabulary range) has no mass: its maximum stays -inf and its sum 0,
   // which the walk's merge weighs 0
-  auto stats = [&](const float (&x)[PER], int kind) __attribute__((always_inline)) {
+  auto local_max = [&](const float (&x)[PER]) __attribute__((always_inline)) {
     float mx = x[0];
 #pragma unroll
     for (int i = 1; i < PER; ++i) mx = fmaxf(mx, x[i]);
-    mx = block_max<kSTWaves>(mx, redf);
+    return mx;
+  };
+  auto local_sum = [&](const float (&x)[PER], float mx) __attribute__((always_inline)) {
     double s = 0.0;
     if (mx != -__builtin_huge_valf()) {
 #pragma unroll
@@ -203,12 +207,41 @@ __global__ __launch_bounds__(kSTThreads) void stree_stats_kernel(STreeArgs a) {
         s += (double)((e_bulk(x[i], mx, a.k2f) + e_bulk(x[i + 1], mx, a.k2f)) +
                       (e_bulk(x[i + 2], mx, a.k2f) + e_bulk(x[i + 3], mx, a.k2f)));
     }
-    s = block_sum<kSTWaves>(s, red);
+    return s;
+  };
+  auto store = [&](int kind, float mx, double s) __attribute__((always_inline)) {
     if (threadIdx.x == 0) {
       const size_t o = ((size_t)kind * a.B * a.T + row) * a.nchunks + ch;
       a.part_m[o] = mx;
       a.part_s[o] = s;
     }
+  };
+  // Block reductions of one value, or of the target and draft chunks' values
+  // side by side (one pair of barriers for both; each value is reduced in the
+  // same order either way).
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  auto block_max2 = [&](float& u, float& v) __attribute__((always_inline)) {
+    u = wave_max(u);
+    v = wave_max(v);
+    __syncthreads();
+    if (lane == 0) { redf[wave] = u; redf[kSTWaves + wave] = v; }
+    __syncthreads();
+    u = redf[0];
+    v = redf[kSTWaves];
+#pragma unroll
+    for (int w = 1; w < kSTWaves; ++w) { u = fmaxf(u, redf[w]); v = fmaxf(v, redf[kSTWaves + w]); }
+  };
+  auto block_sum2 = [&](double& u, double& v) __attribute__((always_inline)) {
+    u = wave_sum(u);
+    v = wave_sum(v);
+    __syncthreads();
+    if (lane == 0) { red[wave] = u; red[kSTWaves + wave] = v; }
+    __syncthreads();
+    double su = 0.0, sv = 0.0;
+#pragma unroll
+    for (int w = 0; w < kSTWaves; ++w) { su += red[w]; sv += red[kSTWaves + w]; }
+    u = su;
+    v = sv;
   };
   float x[PER], y[PER];
   load(a.target + (size_t)row * a.V, x);
@@ -221,9 +254,22 @@ __global__ __launch_bounds__(kSTThreads) void stree_stats_kernel(STreeArgs a) {
     a.gz[ci] = make_float2(a.target[r], a.draft[r]);
   }
   const bool kids = __syncthreads_or(mine);    // uniform
-  if (kids) load(a.draft + (size_t)row * a.V, y);   // in flight during the target's sums
-  stats(x, 0);
-  if (kids) stats(y, 1);
+  if (kids) {
+    // both chunks: maxima side by side, then sums side by side
+    load(a.draft + (size_t)row * a.V, y);
+    float mx = local_max(x), my = local_max(y);
+    block_max2(mx, my);
+    double sx = local_sum(x, mx), sy = local_sum(y, my);
+    block_sum2(sx, sy);
+    store(0, mx, sx);
+    store(1, my, sy);
+  } else {
+    float mx = local_max(x);
+    mx = block_max<kSTWaves>(mx, redf);
+    double sx = local_sum(x, mx);
+    sx = block_sum<kSTWaves>(sx, red);
+    store(0, mx, sx);
+  }
 }
 
 // ---------------------------------------------------------------------------
