@@ -75,6 +75,9 @@ class Flag:
     index: int
     boundary: float
     width: float
+    # "draw" only: every positive-weight token whose interval of u-values
+    # meets [u - width, u + width] (band_tokens)
+    alt_tokens: tuple = ()
 
 
 def row_stats(logits, temperature: float = 1.0):
@@ -189,6 +192,22 @@ def inverse_cdf(weights, u):
     return y, c_before / total, c_y / total
 
 
+def band_tokens(weights_row, u: float, width: float) -> tuple:
+    """Every token a draw within `width` of u may land on: the tokens with
+    positive weight whose interval [C_{j-1}, C_j] / C_{V-1} meets [u - width,
+    u + width] (the decision-precision reading of a draw: the running sums
+    are known only to within the edge widths, so any token the band reaches
+    is a correct outcome, however small its own mass)."""
+    w = np.asarray(weights_row, dtype=np.float64)
+    c = np.cumsum(w)
+    total = c[-1]
+    if not total > 0:
+        return ()
+    hi = c / total
+    lo = np.concatenate([[0.0], hi[:-1]])
+    return tuple(int(j) for j in np.flatnonzero((w > 0) & (lo <= u + width) & (hi >= u - width)))
+
+
 @dataclass
 class ChainResult:
     num_accepted: np.ndarray     # [B] int32
@@ -295,10 +314,14 @@ def chain_accept(target_logits, draft_logits, draft_tokens, u_accept, u_draw,
     e_lo = np.where(y > 0, e_cum[seq, np.maximum(y - 1, 0)], 0.0)
     w_hi = edge_width(hi, e_hi, e_tot, z_tot, band)
     w_lo = edge_width(lo, e_lo, e_tot, z_tot, band)
-    for b in np.flatnonzero(np.abs(u - lo) <= w_lo):
-        flags[b].append(Flag("draw", int(stop[b]), float(lo[b]), float(w_lo[b])))
-    for b in np.flatnonzero(np.abs(u - hi) <= w_hi):
-        flags[b].append(Flag("draw", int(stop[b]), float(hi[b]), float(w_hi[b])))
+    near_lo = np.abs(u - lo) <= w_lo
+    near_hi = np.abs(u - hi) <= w_hi
+    for b in np.flatnonzero(near_lo | near_hi):
+        alts = band_tokens(w[b], float(u[b]), float(max(w_lo[b], w_hi[b])))
+        if near_lo[b]:
+            flags[b].append(Flag("draw", int(stop[b]), float(lo[b]), float(w_lo[b]), alts))
+        if near_hi[b]:
+            flags[b].append(Flag("draw", int(stop[b]), float(hi[b]), float(w_hi[b]), alts))
     num = stop.astype(np.int32)
     col = np.arange(N + 1)[None, :]
     out = np.full((B, N + 1), -1, dtype=np.int32)
@@ -320,9 +343,11 @@ def chain_admissible(target_logits, draft_logits, draft_tokens, u_accept, u_draw
                      temperature: float = 1.0, band: float = BOUNDARY_BAND,
                      depth: int = 3) -> set:
     """The outcomes (num_accepted, out_tokens as a tuple) that sequence b may
-    have under the error model: chain_accept's own, and for every flagged
-    decision the outcome with that decision taken each way (its uniform
-    moved to either side of the boundary), recursively to `depth` levels."""
+    have under the error model: chain_accept's own; for every flagged ratio
+    test the outcome with that test taken each way (its uniform moved to
+    either side of the boundary), recursively to `depth` levels; for a
+    flagged draw every token its band reaches (Flag.alt_tokens: the draw's
+    uniform decides nothing else, so only the drawn token changes)."""
     sl = slice(b, b + 1)
     zp = np.asarray(target_logits)[sl]
     zq = np.asarray(draft_logits)[sl]
@@ -336,6 +361,14 @@ def chain_admissible(target_logits, draft_logits, draft_tokens, u_accept, u_draw
         seen.add(key)
         r = chain_accept(zp, zq, x, ua, ud, temperature, band)
         outcomes.add((int(r.num_accepted[0]), tuple(int(t) for t in r.out_tokens[0])))
+        n = int(r.num_accepted[0])
+        for f in r.flags[0]:
+            if f.kind != "draw":
+                continue
+            for j in f.alt_tokens:
+                toks = [int(t) for t in r.out_tokens[0]]
+                toks[n] = j
+                outcomes.add((n, tuple(toks)))
         if d == 0:
             return
         for f in r.flags[0]:
@@ -554,10 +587,12 @@ def tree_accept_sampled(target_logits, draft_logits, tokens, parents, u_accept, 
         # b = C/total moves by (δC·(1 − b) − b·δ(total − C))/total
         w_hi = band * hi + (1 - hi) * e_hi + hi * (e_cum[-1] - e_hi)
         w_lo = band * lo + (1 - lo) * e_lo + lo * (e_cum[-1] - e_lo)
-        if abs(u - lo) <= w_lo:
-            flags[b].append(Flag("draw", n, float(lo), float(w_lo)))
-        if abs(u - hi) <= w_hi:
-            flags[b].append(Flag("draw", n, float(hi), float(w_hi)))
+        if abs(u - lo) <= w_lo or abs(u - hi) <= w_hi:
+            alts = band_tokens(ref, float(u), float(max(w_lo, w_hi)))
+            if abs(u - lo) <= w_lo:
+                flags[b].append(Flag("draw", n, float(lo), float(w_lo), alts))
+            if abs(u - hi) <= w_hi:
+                flags[b].append(Flag("draw", n, float(hi), float(w_hi), alts))
         accept_len[b] = len(nodes) - 1
         path[b, :len(nodes)] = nodes
         emitted = [int(tok[b, i]) for i in nodes[1:]] + [int(y)]
@@ -570,9 +605,10 @@ def tree_sampled_admissible(target_logits, draft_logits, tokens, parents, u_acce
                             b: int, temperature: float = 1.0, band: float = BOUNDARY_BAND,
                             depth: int = 3) -> set:
     """The outcomes (accept_len, path, out_tokens, as tuples) that sequence b
-    may have under the error model: tree_accept_sampled's own, and for every
-    flagged decision the outcome with that decision taken each way (its
-    uniform moved to either side of the boundary), recursively to `depth`."""
+    may have under the error model: tree_accept_sampled's own; for every
+    flagged ratio test the outcome with that test taken each way (its uniform
+    moved to either side of the boundary), recursively to `depth`; for a
+    flagged draw every token its band reaches (Flag.alt_tokens)."""
     sl = slice(b, b + 1)
     zp = np.asarray(target_logits)[sl]
     zq = np.asarray(draft_logits)[sl]
@@ -588,6 +624,15 @@ def tree_sampled_admissible(target_logits, draft_logits, tokens, parents, u_acce
         r = tree_accept_sampled(zp, zq, tok, par, ua, ud, temperature, band)
         outcomes.add((int(r.accept_len[0]), tuple(int(t) for t in r.path[0]),
                       tuple(int(t) for t in r.out_tokens[0])))
+        n = int(r.accept_len[0])
+        path_t = tuple(int(t) for t in r.path[0])
+        for f in r.flags[0]:
+            if f.kind != "draw":
+                continue
+            for j in f.alt_tokens:
+                toks = [int(t) for t in r.out_tokens[0]]
+                toks[n] = j
+                outcomes.add((n, path_t, tuple(toks)))
         if d == 0:
             return
         for f in r.flags[0]:

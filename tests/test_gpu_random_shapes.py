@@ -92,6 +92,27 @@ def test_chain_acceptance_random_shapes(seed):
     assert ref.near_boundary.sum() <= max(1, 0.25 * B)
 
 
+@pytest.mark.parametrize("B,N,V,tau,seed", [
+    (64, 3, 262144, 1.0, 785),      # 16 statistics chunks per row
+    (15, 3, 262145, 1.5, 786),      # 17: the whole-wave merge
+])
+def test_chain_acceptance_large_vocabularies(B, N, V, tau, seed):
+    """Vocabularies past the largest reference one: many draws land within
+    the float32 band of several CDF edges at once, around tokens narrower
+    than the band, and each must be one of the tokens the band reaches."""
+    dev = device()
+    w = I.WORKLOADS["large_batch_chain"].with_(B=B, T=N + 1, V=V, temperature=tau, seed=seed)
+    d = I.make_chain_inputs(w, dev)
+    num, out = nat.spec_accept_chain(d["target_logits"], d["draft_logits"], d["draft_tokens"],
+                                     d["u_accept"], d["u_draw"], temperature=tau)
+    torch.cuda.synchronize()
+    ref = check_chain(d, num, out, temperature=tau, label=f"chain B={B} N={N} V={V} tau={tau}")
+    # flat rows over a quarter of a million tokens widen the residual's band
+    # (up to 4e-5 relative here): up to 40 % flagged, each held to its
+    # admissible outcomes
+    assert ref.near_boundary.sum() <= max(1, 0.4 * B)
+
+
 @pytest.mark.parametrize("seed", range(6))
 def test_tree_acceptance_random_trees(seed):
     dev = device()

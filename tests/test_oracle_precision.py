@@ -229,6 +229,28 @@ def test_cdf_edge_is_flagged_and_both_tokens_admissible():
     assert chain_admissible(zp, zq, x, ua, np.array([[0.45]]), 0, band=0.0) == {(0, (1,))}
 
 
+def test_draw_band_reaches_a_token_narrower_than_the_band():
+    # p_0 = [0.5, 2e-7, 0.5 - 2e-7]; u just below the edge at 0.5.  The band
+    # around u (width about band·u) reaches token 1 (mass 2e-7, narrower than
+    # the band) and the start of token 2: all three are admissible.  Moving u
+    # twice the width past the edge lands on token 2 and never on token 1.
+    zp = np.log(np.array([[[0.5, 2e-7, 0.5 - 2e-7]]]))
+    zq = np.zeros((1, 0, 3))
+    x = np.zeros((1, 0), dtype=np.int64)
+    ua = np.zeros((1, 0))
+    ud = np.array([[0.5 - 1e-7]])
+    res = chain_accept(zp, zq, x, ua, ud, band=1e-6)
+    assert int(res.out_tokens[0, 0]) == 0 and [f.kind for f in res.flags[0]] == ["draw"]
+    assert chain_admissible(zp, zq, x, ua, ud, 0, band=1e-6) == {(0, (0,)), (0, (1,)), (0, (2,))}
+    # far from the edge: token 0 alone
+    assert chain_admissible(zp, zq, x, ua, np.array([[0.3]]), 0, band=1e-6) == {(0, (0,))}
+    # the same draw at the root of a one-node tree
+    tok = np.array([[0]])
+    par = np.array([[-1]])
+    alts = tree_sampled_admissible(zp, zp, tok, par, np.array([[0.5]]), ud, 0, band=1e-6)
+    assert alts == {(0, (0,), (0,)), (0, (0,), (1,)), (0, (0,), (2,))}
+
+
 def test_residual_near_empty_is_ambiguous_but_identical_rows_are_not():
     rng = np.random.default_rng(15)
     zp = rng.normal(0, 2.0, (2, 2, 50))
