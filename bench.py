@@ -574,7 +574,7 @@ def main():
 
     commit = sampled = None
     if w.kind == "tree":
-        commit = time_commit(step, args.steps)
+        commit = time_commit(step, args.steps, flush)
         sampled = time_sampled_tree(w, dev, args.steps, flush)
 
     cpu = None
