@@ -50,7 +50,7 @@ def attention_case(seed: int):
                 g=g)
 
 
-@pytest.mark.parametrize("seed", range(12))
+@pytest.mark.parametrize("seed", range(40))
 def test_attention_random_shapes(seed):
     dev = device()
     c = attention_case(seed)
@@ -113,13 +113,13 @@ def test_chain_acceptance_large_vocabularies(B, N, V, tau, seed):
     assert ref.near_boundary.sum() <= max(1, 0.4 * B)
 
 
-@pytest.mark.parametrize("seed", range(6))
+@pytest.mark.parametrize("seed", range(24))
 def test_tree_acceptance_random_trees(seed):
     dev = device()
     g = torch.Generator().manual_seed(5000 + seed)
     B = int(torch.randint(1, 17, (1,), generator=g))
     T = int(torch.randint(1, 65, (1,), generator=g))
-    V = [3, 1000, 4097, 32000, 50001, 8][seed]
+    V = [3, 1000, 4097, 32000, 50001, 8][seed % 6]
     par = random_parents(B, T, g)
     logits = torch.randn((B, T, V), generator=g) * 3
     # the first child of each node carries its parent's most likely token with
@@ -148,7 +148,7 @@ def test_tree_acceptance_random_trees(seed):
     np.testing.assert_array_equal(i64(out), ref.out_tokens)
 
 
-@pytest.mark.parametrize("seed", range(8))
+@pytest.mark.parametrize("seed", range(32))
 def test_paged_attention_random_shapes(seed):
     """Paged cache with ragged prefix lengths, random trees or chains, random
     page sizes and layouts, compared element by element with oracle.paged."""
@@ -221,7 +221,7 @@ def test_sampled_tree_acceptance_random_trees(seed):
         assert np.array_equal(out[b, :n], tokens[b, path[b, 1:n + 1]].numpy())
 
 
-@pytest.mark.parametrize("seed", range(6))
+@pytest.mark.parametrize("seed", range(24))
 def test_kv_commit_random_paths(seed):
     """The KV commit of a random root path (a random node and its ancestors) of
     a random tree, bit for bit against oracle.commit: random batch, KV heads,
@@ -257,7 +257,7 @@ def test_kv_commit_random_paths(seed):
     assert np.array_equal(host(v), want_v)
 
 
-@pytest.mark.parametrize("seed", range(6))
+@pytest.mark.parametrize("seed", range(24))
 def test_ngram_random_histories(seed):
     """n-gram drafting on seeded random histories: batch, length (ragged per
     sequence), vocabulary, number of drafts and n-gram range all drawn."""
@@ -266,7 +266,7 @@ def test_ngram_random_histories(seed):
     g = torch.Generator().manual_seed(9000 + seed)
     B = int(torch.randint(1, 33, (1,), generator=g))
     L = int(torch.randint(1, 12000, (1,), generator=g))
-    V = [2, 5, 50, 1000, 32000, 3][seed]
+    V = [2, 5, 50, 1000, 32000, 3][seed % 6]
     N = int(torch.randint(0, 64, (1,), generator=g))
     n_min = int(torch.randint(1, 5, (1,), generator=g))
     n_max = n_min + int(torch.randint(0, 6, (1,), generator=g))
