@@ -221,6 +221,42 @@ def test_sampled_tree_acceptance_random_trees(seed):
         assert np.array_equal(out[b, :n], tokens[b, path[b, 1:n + 1]].numpy())
 
 
+@pytest.mark.parametrize("seed", [1, 8, 24])
+def test_sampled_tree_acceptance_large_vocabularies(seed):
+    """Sampled tree acceptance past 2^17 tokens, where the walk streams each
+    visited row instead of holding it in registers: V = 131071, 262144 and
+    262145 on random trees, every sequence exact or inside its admissible
+    set.  Flat rows over that many tokens widen the float32 band (a sweep of
+    60 such seeds flagged a fifth of the sequences), so up to 40 % may be
+    flagged here."""
+    dev = device()
+    g = torch.Generator().manual_seed(11000 + seed)
+    B = int(torch.randint(1, 7, (1,), generator=g))
+    T = int(torch.randint(1, 65, (1,), generator=g))
+    V = [65537, 131071, 152064, 262144, 262145][seed % 5]
+    tau = [1.0, 0.7, 1.3, 2.0][seed % 4]
+    par = random_parents(B, T, g)
+    target = torch.randn((B, T, V), generator=g) * 2.0
+    draft = target + torch.randn((B, T, V), generator=g) * [1.0, 0.5, 2.0][seed % 3]
+    gumbel = -torch.log(-torch.log(torch.rand((B, T, V), generator=g).clamp_(1e-12, 1 - 1e-7)))
+    pidx = par.clamp(min=0).long()
+    parent_rows = torch.gather(draft, 1, pidx[:, :, None].expand(B, T, V))
+    tokens = torch.argmax(parent_rows / tau + gumbel, dim=2).to(torch.int32)
+    del gumbel, parent_rows
+    u = lambda: ((torch.randint(1, 1 << 24, (B, T), generator=g).double()   # noqa: E731
+                  / float(1 << 24)).float())
+    ua, ud = u(), u()
+    d = dict(target_logits=target, draft_logits=draft, tokens=tokens, parents=par,
+             u_accept=ua, u_draw=ud)
+    al, path, out = nat.spec_accept_tree_sampled(*(d[k].to(dev) for k in (
+        "target_logits", "draft_logits", "tokens", "parents", "u_accept", "u_draw")),
+        temperature=tau)
+    torch.cuda.synchronize()
+    ref = check_tree_sampled(d, al, path, out, temperature=tau,
+                             label=f"sampled tree seed {seed} B={B} T={T} V={V} tau={tau}")
+    assert ref.near_boundary.sum() <= max(1, 0.4 * B)
+
+
 @pytest.mark.parametrize("seed", range(24))
 def test_kv_commit_random_paths(seed):
     """The KV commit of a random root path (a random node and its ancestors) of
