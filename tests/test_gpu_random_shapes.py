@@ -113,13 +113,14 @@ def test_chain_acceptance_large_vocabularies(B, N, V, tau, seed):
     assert ref.near_boundary.sum() <= max(1, 0.4 * B)
 
 
-@pytest.mark.parametrize("seed", range(24))
-def test_tree_acceptance_random_trees(seed):
+def tree_acceptance_case(seed: int, vocabularies):
+    """Greedy tree acceptance of a seeded random tree, bit for bit against
+    oracle.tree_accept; V = vocabularies[seed % len(vocabularies)]."""
     dev = device()
     g = torch.Generator().manual_seed(5000 + seed)
     B = int(torch.randint(1, 17, (1,), generator=g))
     T = int(torch.randint(1, 65, (1,), generator=g))
-    V = [3, 1000, 4097, 32000, 50001, 8][seed % 6]
+    V = vocabularies[seed % len(vocabularies)]
     par = random_parents(B, T, g)
     logits = torch.randn((B, T, V), generator=g) * 3
     # the first child of each node carries its parent's most likely token with
@@ -146,6 +147,17 @@ def test_tree_acceptance_random_trees(seed):
     np.testing.assert_array_equal(i64(al), ref.accept_len)
     np.testing.assert_array_equal(i64(path), ref.path)
     np.testing.assert_array_equal(i64(out), ref.out_tokens)
+
+
+@pytest.mark.parametrize("seed", range(24))
+def test_tree_acceptance_random_trees(seed):
+    tree_acceptance_case(seed, [3, 1000, 4097, 32000, 50001, 8])
+
+
+@pytest.mark.parametrize("seed", [1, 2])
+def test_tree_acceptance_large_vocabularies(seed):
+    """32 and 33 argmax chunks per row (V = 262144, 262145)."""
+    tree_acceptance_case(seed, [131071, 262144, 262145, 152064, 65536, 100003])
 
 
 @pytest.mark.parametrize("seed", range(32))
