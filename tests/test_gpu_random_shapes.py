@@ -93,6 +93,24 @@ def test_chain_acceptance_random_shapes(seed):
 
 
 @pytest.mark.parametrize("B,N,V,tau,seed", [
+    (46, 11, 4099, 0.05, 805),      # near one-hot rows: tiny ratios and residuals
+    (46, 9, 131071, 0.05, 865),
+    (54, 4, 40000, 20.0, 829),      # near-uniform rows: target and draft almost equal
+])
+def test_chain_acceptance_extreme_temperatures(B, N, V, tau, seed):
+    """Temperatures far from 1 on the chain: every sequence exact or inside
+    its admissible set, at most a quarter flagged."""
+    dev = device()
+    w = I.WORKLOADS["large_batch_chain"].with_(B=B, T=N + 1, V=V, temperature=tau, seed=seed)
+    d = I.make_chain_inputs(w, dev)
+    num, out = nat.spec_accept_chain(d["target_logits"], d["draft_logits"], d["draft_tokens"],
+                                     d["u_accept"], d["u_draw"], temperature=tau)
+    torch.cuda.synchronize()
+    ref = check_chain(d, num, out, temperature=tau, label=f"chain B={B} N={N} V={V} tau={tau}")
+    assert ref.near_boundary.sum() <= max(1, 0.25 * B)
+
+
+@pytest.mark.parametrize("B,N,V,tau,seed", [
     (64, 3, 262144, 1.0, 785),      # 16 statistics chunks per row
     (15, 3, 262145, 1.5, 786),      # 17: the whole-wave merge
 ])
