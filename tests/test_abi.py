@@ -1,7 +1,6 @@
 """The C-ABI library on the host: it loads, exports every function
 include/spec_verify.h declares, and rejects bad arguments before launching
 anything (no GPU needed: every call here fails validation or is empty)."""
-import ctypes
 import os
 import re
 import subprocess

@@ -13,7 +13,6 @@ spanned only their enumerators; they now span every int32.)
 import os
 import subprocess
 
-import pytest
 
 from verify_pass_rejection_amd import build as B
 

@@ -20,7 +20,6 @@ positions, so a bonus token from p_N when all drafts are kept).
 import itertools
 
 import numpy as np
-import pytest
 from scipy import stats
 from scipy.special import softmax as sp_softmax
 

@@ -9,7 +9,6 @@ the pins.
 """
 import numpy as np
 import pytest
-import torch
 
 import oracle.paged as OP
 from oracle.attention import verify_attention
