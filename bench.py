@@ -499,6 +499,55 @@ def step_figures(w, step, t):
     }
 
 
+def time_graph_replay(step, steps: int):
+    """Back-to-back steps (attention then acceptance) with the inputs resident,
+    eager against replays of the step captured once into a HIP graph through
+    torch's graph API: one event pair around `steps` steps, in three
+    alternating rounds, median per-step time of each.  On launch-bound shapes
+    the host's launches set the eager rate and a replay removes them.  The
+    replay's outputs are compared bit for bit with an eager step's."""
+    import torch
+    side = torch.cuda.Stream()                  # default priority
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()                                  # first run outside the capture
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    torch.cuda.synchronize()
+    for _ in range(3):
+        g.replay()
+        step()
+    torch.cuda.synchronize()
+
+    def loop(fn):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(steps):
+            fn()
+        b.record()
+        b.synchronize()
+        return a.elapsed_time(b) * 1e3 / steps
+
+    eager, replay = [], []
+    for _ in range(3):
+        eager.append(loop(step))
+        replay.append(loop(g.replay))
+    g.replay()
+    torch.cuda.synchronize()
+    replayed = [t.clone() for t in (step.out, step.num, step.tok, step.path)]
+    step()
+    torch.cuda.synchronize()
+    same = all(torch.equal(a, b) for a, b in zip(replayed, (step.out, step.num, step.tok,
+                                                            step.path)))
+    del g
+    return {"eager_us": round(pct(eager, 0.5), 2), "graph_replay_us": round(pct(replay, 0.5), 2),
+            "steps_per_round": steps, "bitwise_equal_to_eager": bool(same),
+            "note": "back-to-back steps, inputs cache-resident"}
+
+
 def measure_config(name, dev, steps: int, warmup: int, with_alpha: bool):
     """One of the other reference workloads at its full size, cache flushed
     between steps: the step figures, alpha on chains, and for trees the KV
@@ -517,6 +566,7 @@ def measure_config(name, dev, steps: int, warmup: int, with_alpha: bool):
         out["note"] = "launch-bound correctness workload (1 MB of attention bytes)"
     if with_alpha and w.kind == "chain":
         out.update(measure_alpha(w, dev, step, max(40, steps), flush))
+    out["back_to_back"] = time_graph_replay(step, steps)
     if w.kind == "tree":
         out["kv_commit"] = time_commit(step, steps, flush)
         out["sampled_tree_acceptance"] = time_sampled_tree(w, dev, steps, flush)
