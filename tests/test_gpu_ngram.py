@@ -67,3 +67,21 @@ def test_degenerate_histories():
     ctx = torch.arange(0, 3 * 5000, dtype=torch.int32).view(3, 5000)
     compare(ctx.to(dev), torch.full((3,), 5000, dtype=torch.int32).to(dev), 8, 1, 4,
             label="no repeats")
+
+
+@pytest.mark.parametrize("ctx_len,V,N,n_min,n_max", [
+    (32768, 50, 8, 1, 4),        # the longest history one block holds
+    (32769, 50, 8, 1, 4),        # one token more: the tiled two-kernel path
+    (40000, 7, 63, 2, 16),       # tiled, the largest n-gram and the most drafts
+    (32768, 2, 5, 1, 16),        # one block, two tokens: matches at almost every end
+])
+def test_history_length_paths(ctx_len, V, N, n_min, n_max):
+    """Histories up to 32768 tokens are scanned by one block per sequence out
+    of LDS, longer ones by tiles across blocks; both against the oracle."""
+    dev = device()
+    w = I.WORKLOADS["large_batch_chain"].with_(B=6, ctx=ctx_len, V=V, seed=61)
+    ctx, lens = I.make_ngram_inputs(w, dev)
+    compare(ctx, lens, N, n_min, n_max, label=f"L={ctx_len} V={V}")
+    compare(ctx, lens, N, n_min, n_max, label=f"L={ctx_len} V={V} lengths NULL",
+            pass_lens=False)
+
